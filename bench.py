@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Bandwidth bench of the temperature softmax over the vocabulary on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one ts_softmax call over one batch: B=64 rows of V=262144 float32
+logits (N(0,1)*4, temperatures U[0.5, 1.5), one quarter of the rows each
+unmasked / first 16384 columns -inf / a random 20000-column -inf block / all
+but 3 ids -inf). Inputs are resident in HBM before timing. Calls rotate over
+enough buffer sets (>= 512 MiB of logits + probs) that each call finds its
+logits outside the 256 MiB Infinity Cache: the headline is this cold rate.
+
+Prints one JSON line. `value` is the algorithmic HBM rate 2*B*V*4 bytes per
+call over the timed region (GB/s); `roofline` compares the per-launch rate of
+the dominant kernel with MI355X's 8 TB/s; `cpu_baseline` times the float64
+oracle on the host over the same workload.
+
+Extra mode: `python bench.py --summarize-counters FETCH_DIR WRITE_DIR` turns
+two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench into the
+per-dispatch counter summary under profiles/ that the JSON line's
+`roofline.traffic` is read from.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "µs/call and HBM GB/s (% of peak) for B×V fp32 temperature softmax"
+DEFAULT_WORKLOAD = "B64_V262144_masked_quarters"
+COLD_FOOTPRINT = 512 << 20     # >= 2x the 256 MiB Infinity Cache
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "temperature_softmax_vocabulary_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_file(kernel_tag: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"{kernel_tag}_{workload}_hbm_counters.txt")
+
+
+def read_traffic(kernel_tag: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or was taken from different kernel sources."""
+    path = counters_file(kernel_tag, workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------
+# counters summary (host-side parsing of rocprofv3 CSV output)
+# ----------------------------------------------------------------------------
+
+def _counter_rows(d: str):
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter: str, name_part: str):
+    by_dispatch = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or name_part not in r.get("Kernel_Name", ""):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        by_dispatch[key] = by_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    vals = list(by_dispatch.values())
+    return (statistics.mean(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, kernel_name: str, kernel_tag: str,
+                       command: str) -> str:
+    from temperature_softmax_vocabulary_amd import workloads
+    c = workloads.CONFIGS[workload]
+    n_bytes = c["B"] * c["V"] * 4
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    f_k, nf = _per_dispatch(fr, "FETCH_SIZE", kernel_name)
+    w_k, nw = _per_dispatch(wr, "WRITE_SIZE", kernel_name)
+    f_c, ncf = _per_dispatch(fr, "FETCH_SIZE", "ts_copy_vec")
+    w_c, ncw = _per_dispatch(wr, "WRITE_SIZE", "ts_copy_vec")
+    if None in (f_k, w_k, f_c, w_c):
+        raise SystemExit(f"missing counters: kernel fetch={f_k} write={w_k} copy fetch={f_c} write={w_c}")
+    # The copy reads and writes exactly n_bytes each: KiB-per-dispatch -> bytes factor.
+    ff = n_bytes / (f_c * 1024.0)
+    wf = n_bytes / (w_c * 1024.0)
+    fetch_b = f_k * 1024.0 * ff
+    write_b = w_k * 1024.0 * wf
+    out = counters_file(kernel_tag, workload)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(out, "w") as f:
+        f.write(f"# HBM byte counters per dispatch for {kernel_name} on {workload}\n")
+        f.write(f"# rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, on: {command}\n")
+        f.write("# raw values in KiB per dispatch; scaled by a plain copy of the same bytes\n")
+        f.write(f"kernel_source_sha256={kernel_source_hash()}\n")
+        f.write(f"kernel={kernel_name}\n")
+        f.write(f"dispatches_fetch={nf}\ndispatches_write={nw}\n")
+        f.write(f"fetch_kib={f_k:.1f}\nwrite_kib={w_k:.1f}\n")
+        f.write(f"copy_kernel=ts_copy_vec\ncopy_dispatches={ncf},{ncw}\n")
+        f.write(f"copy_bytes_each_way={n_bytes}\ncopy_fetch_kib={f_c:.1f}\ncopy_write_kib={w_c:.1f}\n")
+        f.write(f"fetch_factor={ff:.4f}\nwrite_factor={wf:.4f}\n")
+        f.write(f"fetch_bytes_per_launch={fetch_b:.0f}\nwrite_bytes_per_launch={write_b:.0f}\n")
+        f.write(f"traffic_bytes_per_launch={fetch_b + write_b:.0f}\n")
+        f.write(f"algorithmic_bytes_per_launch={2 * n_bytes}\n")
+        f.write(f"traffic_over_algorithmic={(fetch_b + write_b) / (2 * n_bytes):.4f}\n")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------
+
+def _elapsed_us(torch, fn, n):
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for i in range(n):
+        fn(i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / n
+
+
+def cpu_baseline(w, target_s: float):
+    """The float64 oracle, as it stands, on the host over the same workload."""
+    from oracle import softmax_ref
+    bytes_per_call = 2 * w.B * w.V * 4
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        softmax_ref(w.logits, w.temps)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    gbs = bytes_per_call * reps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full {w.name} workload (B={w.B}, V={w.V}), {reps} calls in {el:.1f} s, "
+                      f"numpy float64, one thread; us/call {el / reps * 1e6:.0f}"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--variant", type=int, default=0, help="force a work split (0 = library's choice)")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-extras", action="store_true", help="skip the hot/copy/sample side measurements")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--counters-command", default="python bench.py --steps 200 --warmup 20 --no-cpu-baseline")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the softmax is sharded across GPUs by row or by vocabulary slice; "
+              "this build measures one GPU's share)", file=sys.stderr)
+        return 2
+
+    import torch
+    import temperature_softmax_vocabulary_amd as tsv
+    from temperature_softmax_vocabulary_amd import workloads
+
+    if args.summarize_counters:
+        v, c = (args.variant, args.chunk) if args.variant else (None, None)
+        cfg = workloads.CONFIGS[args.workload]
+        plan = tsv.ts_plan(cfg["B"], cfg["V"]) if v is None else (v, c)
+        name, tag = _kernel_names(tsv, plan)
+        print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
+                                 name, tag, args.counters_command))
+        return 0
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.make_config(args.workload)
+    B, V = w.B, w.V
+    bytes_per_call = 2 * B * V * 4
+    nsets = max(2, math.ceil(COLD_FOOTPRINT / bytes_per_call))
+    xs = [torch.from_numpy(w.logits).to(dev) for _ in range(nsets)]
+    ts = [torch.from_numpy(w.temps).to(dev) for _ in range(nsets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+    plan = tsv.ts_plan(B, V) if not args.variant else (args.variant, args.chunk)
+    kname, ktag = _kernel_names(tsv, plan)
+
+    def step(i):
+        j = i % nsets
+        if args.variant:
+            tsv.ts_softmax_variant(xs[j], ts[j], args.variant, args.chunk, out=ys[j])
+        else:
+            tsv.ts_softmax(xs[j], ts[j], out=ys[j])
+
+    tsv.ts_reserve(B, V)
+    print(f"[bench] workload={w.name} plan={plan} sets={nsets} warmup={args.warmup} steps={args.steps}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    us = _elapsed_us(torch, step, args.steps)            # the timed region: exactly K steps
+    errs = tsv.ts_device_errors()
+    y = ys[(args.steps - 1) % nsets]
+    rowsum = y.double().sum(dim=1)
+    sane = bool(torch.isfinite(y).all().item()) and float((rowsum - 1).abs().max().item()) < 1e-5
+    print(f"[bench] cold {us:.2f} us/call, device errors {errs}, outputs sane {sane}", file=sys.stderr, flush=True)
+
+    gbs = bytes_per_call / us / 1e3
+    launches_per_call = 2 if plan[0] == tsv.TS_VARIANT_SPLIT else 1
+    traffic = read_traffic(ktag, w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1000.0, 6),
+        "us_per_call": round(us, 3),
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "V": V, "masks": "quarters: none/first16384/block20000/allowed3",
+                   "rotating_sets": nsets, "variant": tsv.VARIANT_NAMES[plan[0]], "chunk": plan[1],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": kname,
+                     "achieved": round(bytes_per_call / launches_per_call / us / 1e3 * launches_per_call, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic)},
+        "outputs_sane": sane,
+    }
+
+    if not args.no_extras:
+        extras = {}
+        # hot: the same buffers every call (how the page timed, graph replays of one input)
+        def hot(i):
+            tsv.ts_softmax(xs[0], ts[0], out=ys[0])
+        for i in range(20):
+            hot(i)
+        extras["hot_us_per_call"] = round(_elapsed_us(torch, hot, 200), 3)
+        # same bytes through a plain streaming copy, cold (practical ceiling)
+        def cp(i):
+            j = i % nsets
+            tsv.ts_copy_f32(xs[j], ys[j])
+        for i in range(20):
+            cp(i)
+        cus = _elapsed_us(torch, cp, args.steps)
+        extras["copy_us_per_call"] = round(cus, 3)
+        extras["copy_GBps"] = round(bytes_per_call / cus / 1e3, 1)
+        extras["softmax_over_copy"] = round(cus / us, 4)
+        # graph replay of the same rotating calls (launch gaps removed)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        tsv.ts_reserve(B, V, stream=s)
+        with torch.cuda.stream(s):
+            for i in range(nsets):
+                step(i)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(nsets * 8):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        reps = 5
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        extras["graph_us_per_call"] = round(e0.elapsed_time(e1) * 1000.0 / (reps * nsets * 8), 3)
+        # ts_sample on the same rows, 64 draws each (not part of the metric)
+        u = torch.from_numpy(w.uniforms).to(dev)
+        ids = torch.empty((B, w.uniforms.shape[1]), dtype=torch.int32, device=dev)
+        extras["sample_us_per_call"] = round(_elapsed_us(torch, lambda i: tsv.ts_sample(ys[0], u, out_ids=ids), 50), 3)
+        dp = torch.cuda.get_device_properties(dev)
+        extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
+                            "gcn_arch": getattr(dp, "gcnArchName", "")}
+        result["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _kernel_names(tsv, plan):
+    """(kernel-name substring as rocprofv3 prints it, file tag) for a plan."""
+    v, c = plan
+    if v == tsv.TS_VARIANT_FUSED:
+        return f"ts_fused<{c // 1024}, true>", f"ts_fused_c{c}"
+    if v == tsv.TS_VARIANT_SPLIT:
+        return f"ts_split_finalize_write<{c // 1024}, true>", f"ts_split_c{c}"
+    return "ts_rowwise", "ts_rowwise"
+
+
+if __name__ == "__main__":
+    sys.exit(main())

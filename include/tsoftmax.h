@@ -1,0 +1,164 @@
+/*
+ * tsoftmax: temperature softmax over an LLM vocabulary, and inverse-CDF token
+ * draws, for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the pull-request page "fix(kernel): avoid nan in
+ * triton sampling softmax when a chunk starts with -inf" (FreeToken pull
+ * request 654).
+ *  - Test paragraph: every row b of the logits is divided by its own
+ *    temperature t[b] and normalised with a softmax over the vocabulary.
+ *  - Bug and fix paragraphs: masked logits are -inf; a column chunk whose
+ *    first block is all -inf must add nothing to its row (shift by 0 while the
+ *    running max is still -inf) instead of turning the row into NaN, and a
+ *    fully masked chunk contributes 0 to the row's rescaled sum.
+ *  - Scope paragraph and the sampling row of the results table: the
+ *    probabilities feed a draw of token ids that must always land on an
+ *    allowed (finite-logit) id.
+ *
+ * All entry points are C functions on plain pointers and sizes. Every array
+ * is owned by the caller and lives in device memory of the current HIP device
+ * (except where a pointer is documented as host memory). Calls are
+ * asynchronous on `stream` (NULL = the default stream): they enqueue kernels
+ * and return without synchronising or reading device memory on the host.
+ * Calls on one stream are ordered; calls on different streams may run
+ * concurrently and each stream gets its own small workspace.
+ *
+ * Thread safety: all functions may be called from several host threads.
+ */
+#ifndef TSOFTMAX_H_
+#define TSOFTMAX_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSOFTMAX_ABI_VERSION 1
+
+typedef enum ts_status {
+    TS_OK = 0,
+    /* A pointer, size or alias rule below was broken. Nothing was launched. */
+    TS_ERR_INVALID_ARGUMENT = 1,
+    /* The HIP runtime reported an error (launch or query). */
+    TS_ERR_HIP = 2,
+    /* The library could not allocate its workspace. */
+    TS_ERR_OUT_OF_MEMORY = 3,
+    /* The stream is being captured into a graph and the call needs a larger
+     * workspace than ts_reserve() set aside for it; no allocation is made
+     * during capture. Nothing was launched. */
+    TS_ERR_NOT_RESERVED = 4,
+    /* A kernel's bounded wait for the other chunks of its row ran out
+     * (reported by ts_device_errors only). The rows it touched are invalid. */
+    TS_ERR_SYNC_TIMEOUT = 5
+} ts_status;
+
+/* How ts_softmax_variant splits the work (the method's chunking, bug
+ * paragraph: one program per row and column chunk, then a finalize).
+ *   TS_VARIANT_AUTO    - pick from (B, V) with the built-in table (ts_plan).
+ *   TS_VARIANT_SPLIT   - two kernels: per-chunk (max, scaled sum) partials,
+ *                        then a finalize fused into the write of the probs.
+ *                        Reads the logits twice.
+ *   TS_VARIANT_ROWWISE - one workgroup per row, no partials. Reads the logits
+ *                        once when the row fits in the workgroup's registers,
+ *                        else twice.
+ *   TS_VARIANT_FUSED   - one kernel: per-chunk partials are exchanged through
+ *                        a per-row arrival counter while each workgroup keeps
+ *                        its chunk in registers, then the probs are written.
+ *                        Reads the logits once. */
+typedef enum ts_variant {
+    TS_VARIANT_AUTO = 0,
+    TS_VARIANT_SPLIT = 1,
+    TS_VARIANT_ROWWISE = 2,
+    TS_VARIANT_FUSED = 3
+} ts_variant;
+
+/*
+ * probs[b, :] = softmax(logits[b, :] / temps[b]) for b in [0, B).
+ *
+ * logits : [B, V] float32, row-major, contiguous (row pitch V elements).
+ *          Entries are finite or -inf (masked). Each row must keep at least
+ *          one finite entry; a row of only -inf gives unspecified output.
+ * temps  : [B] float32, every value finite and > 0 (not checked: checking
+ *          would need a device read).
+ * out    : [B, V] float32, row-major, contiguous. out == logits (exact
+ *          alias, in place) is allowed; any other overlap of out with logits
+ *          or temps is rejected.
+ * Result : for a row with at least one finite logit every output is finite,
+ *          a -inf logit gives exactly 0, and the row sums to 1 within float32
+ *          rounding. No alignment is required; 16-byte aligned pointers with
+ *          V % 4 == 0 take the vector-load path.
+ * Errors : TS_ERR_INVALID_ARGUMENT for B < 0, V < 1, V > INT32_MAX,
+ *          B*V*4 not addressable, a NULL pointer when B > 0, or an illegal
+ *          overlap. B == 0 is a no-op returning TS_OK.
+ *          TS_ERR_NOT_RESERVED, TS_ERR_OUT_OF_MEMORY, TS_ERR_HIP as above.
+ */
+ts_status ts_softmax(const float* logits, const float* temps, int64_t B, int64_t V,
+                     float* out, hipStream_t stream);
+
+/*
+ * ts_softmax with the work split forced: `variant` is a ts_variant and
+ * `chunk` the columns per workgroup (one of 1024, 2048, 4096, 8192, 16384 for
+ * SPLIT and FUSED; ignored by ROWWISE; 0 = the table's choice). Same result
+ * contract as ts_softmax. Meant for tests and tuning; a combination the
+ * library cannot run (e.g. FUSED with more chunks per row than the GPU can
+ * hold at once) returns TS_ERR_INVALID_ARGUMENT.
+ */
+ts_status ts_softmax_variant(const float* logits, const float* temps, int64_t B, int64_t V,
+                             float* out, int32_t variant, int32_t chunk, hipStream_t stream);
+
+/*
+ * The work split ts_softmax would use for (B, V) on the current device, for a
+ * 16-byte aligned call with V % 4 == 0. Host only: launches nothing.
+ * variant, chunk : host pointers, written on TS_OK.
+ */
+ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
+
+/*
+ * Inverse-CDF token draws from caller-supplied uniforms.
+ *
+ * probs    : [B, V] float32 row-major contiguous, non-negative rows (normally
+ *            ts_softmax outputs). Entries that are not > 0 (0, negative, NaN)
+ *            are never drawn.
+ * uniforms : [B, K] float32. Each u is clamped to [0, 1]; NaN counts as 0.
+ * out_ids  : [B, K] int32. For each (b, k): with C the row's inclusive
+ *            prefix sums and target = u * C[V-1], the smallest id j with
+ *            C[j] > target; for u = 1 the last id with a positive entry.
+ *            The prefix sums are formed exactly, in 64-bit fixed point at a
+ *            per-row power-of-two scale, so the id is always one with a
+ *            positive probability. A row with no positive entry gives -1.
+ * Errors   : TS_ERR_INVALID_ARGUMENT for B < 0, K < 0, V < 1,
+ *            V > INT32_MAX, a NULL pointer when B*K > 0, or out_ids overlapping
+ *            probs or uniforms. B == 0 or K == 0 is a no-op.
+ */
+ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_t V, int64_t K,
+                    int32_t* out_ids, hipStream_t stream);
+
+/*
+ * Set aside the workspace for any later call with B <= max_B and
+ * V <= max_V on `stream`, so that those calls allocate nothing (needed
+ * before capturing them into a HIP graph). Allocates and clears device
+ * memory; must not itself be called while `stream` is capturing.
+ */
+ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream);
+
+/*
+ * Synchronise `stream`, then report and clear the device-side error flags of
+ * its workspace. *flags (host pointer) receives the raw bits (bit 0: a fused
+ * kernel's bounded wait ran out). Returns TS_ERR_SYNC_TIMEOUT if bit 0 was
+ * set, else TS_OK.
+ */
+ts_status ts_device_errors(hipStream_t stream, uint32_t* flags);
+
+/* Static text for a status code (never NULL). */
+const char* ts_status_string(ts_status status);
+
+/* TSOFTMAX_ABI_VERSION of the built library. */
+int32_t ts_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSOFTMAX_H_ */

@@ -1,0 +1,40 @@
+/*
+ * Measurement and failure-path hooks of libtsoftmax. Not part of the method:
+ * they exist so that the softmax's bandwidth can be put next to a plain copy
+ * of the same bytes, and so that the bounded wait of the fused kernel can be
+ * exercised from the host without any kernel faulting or hanging.
+ */
+#ifndef TSOFTMAX_MEASURE_H_
+#define TSOFTMAX_MEASURE_H_
+
+#include "tsoftmax.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * dst[i] = src[i] for i in [0, n): a streaming float32 copy on `stream`
+ * (16-byte loads and stores when both pointers are 16-byte aligned). It reads
+ * n*4 bytes and writes n*4 bytes, the same algorithmic traffic as ts_softmax
+ * on n = B*V elements, and serves as the practical bandwidth ceiling and as
+ * the calibration kernel for the HBM byte counters.
+ * Errors: TS_ERR_INVALID_ARGUMENT for n < 0, NULL pointers with n > 0, or
+ * overlapping ranges.
+ */
+ts_status ts_copy_f32(const float* src, float* dst, int64_t n, hipStream_t stream);
+
+/*
+ * Number of polls (each a short sleep plus one load) a fused-kernel
+ * workgroup makes while waiting for the rest of its row before it gives up,
+ * raises bit 0 of the device error flags and carries on. 0 restores the
+ * default (about 2^18 polls, far beyond any legal wait). Takes effect for
+ * launches made after the call, on every device. For failure-path tests only.
+ */
+ts_status ts_debug_set_spin_limit(uint32_t polls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSOFTMAX_MEASURE_H_ */

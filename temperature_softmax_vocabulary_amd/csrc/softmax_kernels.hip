@@ -1,0 +1,342 @@
+// Temperature softmax over the vocabulary: HIP kernels for gfx950.
+//
+// Method: the pull-request page "fix(kernel): avoid nan in triton sampling
+// softmax when a chunk starts with -inf" (FreeToken pull request 654).
+//  - Test paragraph: probs[b, :] = softmax(logits[b, :] / t[b]).
+//  - Bug paragraph: the work is split by row and column chunk; each chunk
+//    keeps a running max m and a sum of exponentials l relative to it, and a
+//    finalize step combines the chunk partials with a global rescale.
+//  - Fix paragraph: while a max is still -inf the shift is 0, so an all -inf
+//    block adds 0, a fully masked chunk stores pl = 0, and its rescale term
+//    0 * exp(-inf - gm) is 0 whenever the row has a finite logit.
+//
+// Three ways to split the work, all with the same per-element arithmetic:
+//  split   : ts_split_partials writes (pm, pl) per (row, chunk); then
+//            ts_split_finalize_write combines a row's partials and writes the
+//            chunk's probs (finalize fused into the write; logits read twice).
+//  fused   : one kernel; each workgroup keeps its chunk's exponentials in
+//            registers, publishes (pm, pl), waits for the row's other chunks
+//            on a per-row arrival counter, then writes (logits read once).
+//  rowwise : one workgroup per row; the row sits in registers when it fits
+//            (read once), else an online (m, l) sweep and a write sweep.
+#include "ts_device.h"
+#include "ts_launch.h"
+
+namespace tsk {
+
+namespace {
+
+constexpr int NT = kChunkThreads;      // 256 lanes = 4 waves
+constexpr int NW = NT / kWave;
+
+__device__ __forceinline__ float2 load_partial(const float2* p) { return *p; }
+
+// ---------------------------------------------------------------------------
+// split, kernel 1: one workgroup per (row, chunk) -> (pm, pl)
+// ---------------------------------------------------------------------------
+template <int F, bool VEC>
+__global__ __launch_bounds__(NT) void ts_split_partials(SoftmaxArgs a) {
+    __shared__ float red[NW];
+    constexpr int C = NT * 4 * F;
+    const int64_t item = blockIdx.x;
+    const int64_t row = item / a.nch;
+    const int64_t c = item - row * a.nch;
+    const float k = exp2_scale(a.temps[row]);
+
+    float x[4 * F];
+    load_chunk<NT, F, VEC, false>(a.logits + row * a.V, c * C, a.V, x);
+
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4 * F; ++i) m = fmaxf(m, x[i]);
+    const float pm = block_reduce<MaxOp, NW>(m, red);
+    const float sh = guarded_shift(pm);
+    float l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4 * F; ++i) l += exp2_hw((x[i] - sh) * k);
+    const float pl = block_reduce<SumOp, NW>(l, red);
+    if (threadIdx.x == 0) a.part[item] = make_float2(pm, pl);
+}
+
+// Combine a row's partials: gm = max pm, gl = sum pl * exp2((pm - gm) k), with
+// a fully masked chunk (pm = -inf, pl = 0) contributing exactly 0.
+__device__ __forceinline__ void combine_row(const float2* __restrict__ part, int64_t nch, float k,
+                                            float* red, float& gsh, float& r) {
+    float m = kNegInf;
+    for (int64_t i = threadIdx.x; i < nch; i += NT) m = fmaxf(m, load_partial(part + i).x);
+    const float gm = block_reduce<MaxOp, NW>(m, red);
+    gsh = guarded_shift(gm);
+    float l = 0.0f;
+    for (int64_t i = threadIdx.x; i < nch; i += NT) {
+        const float2 p = load_partial(part + i);
+        l += (p.x == kNegInf) ? 0.0f : p.y * exp2_hw((p.x - gsh) * k);
+    }
+    const float gl = block_reduce<SumOp, NW>(l, red);
+    r = 1.0f / gl;
+}
+
+// ---------------------------------------------------------------------------
+// split, kernel 2: finalize fused into the write of the probs
+// ---------------------------------------------------------------------------
+template <int F, bool VEC>
+__global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
+    __shared__ float red[NW];
+    constexpr int C = NT * 4 * F;
+    const int64_t item = blockIdx.x;
+    const int64_t row = item / a.nch;
+    const int64_t c = item - row * a.nch;
+    const float k = exp2_scale(a.temps[row]);
+
+    float x[4 * F];
+    load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x);   // last use of logits
+
+    float gsh, r;
+    combine_row(a.part + row * a.nch, a.nch, k, red, gsh, r);
+#pragma unroll
+    for (int i = 0; i < 4 * F; ++i) x[i] = exp2_hw((x[i] - gsh) * k) * r;
+    store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+}
+
+// ---------------------------------------------------------------------------
+// fused: one read of the logits.
+//
+// Workgroup w handles items w, w + gridDim.x, ... (item = row * nch + chunk).
+// The host launches at most as many workgroups as the device holds at once and
+// at least nch of them, so every chunk of the lowest unfinished row is always
+// either done or resident and waiting: the row completes and no wait can
+// deadlock. Each wait is still bounded (spin_limit polls); running out raises
+// bit 0 of *err instead of hanging.
+//
+// Exchange per row (agent scope, so it holds across the XCDs' separate L2s):
+//  lane 0 stores (pm, pl), reads gen[row], then increments cnt[row] with
+//  acq_rel. The workgroup that brings cnt to nch resets it to 0 and bumps
+//  gen[row] with release. Every lane of wave 0 then polls gen[row] with
+//  acquire until it differs from the value read before arriving, which orders
+//  all of the row's partial stores before wave 0's reads of them. The counter
+//  is back at 0 when the kernel ends, so the next launch needs no clearing.
+// ---------------------------------------------------------------------------
+template <int F>
+struct FusedOcc { static constexpr int waves_per_eu = F <= 8 ? 8 : 4; };
+
+template <int F, bool VEC>
+__global__ __launch_bounds__(NT, FusedOcc<F>::waves_per_eu) void ts_fused(SoftmaxArgs a) {
+    __shared__ float red[NW];
+    __shared__ float chunk_scale;
+    constexpr int C = NT * 4 * F;
+    const int lane = threadIdx.x;
+
+    for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+        const int64_t row = item / a.nch;
+        const int64_t c = item - row * a.nch;
+        const float k = exp2_scale(a.temps[row]);
+
+        float x[4 * F];
+        load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x);
+
+        float m = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4 * F; ++i) m = fmaxf(m, x[i]);
+        const float pm = block_reduce<MaxOp, NW>(m, red);
+        const float sh = guarded_shift(pm);
+        float l = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4 * F; ++i) {
+            x[i] = exp2_hw((x[i] - sh) * k);      // kept: the probs are x[i] * scale
+            l += x[i];
+        }
+        const float pl = block_reduce<SumOp, NW>(l, red);
+
+        if (lane < kWave) {
+            uint32_t* cnt = a.cnt + row;
+            uint32_t* gen = a.gen + row;
+            uint32_t g0 = 0;
+            if (lane == 0) {
+                a.part[item] = make_float2(pm, pl);
+                g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t before =
+                    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                if (before + 1 == static_cast<uint32_t>(a.nch)) {
+                    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            g0 = __builtin_amdgcn_readfirstlane(g0);
+            uint32_t polls = 0;
+            while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+                if (++polls > a.spin_limit) {
+                    if (lane == 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            // Wave 0 combines the row's partials (nch <= the resident grid).
+            const float2* part = a.part + row * a.nch;
+            float mm = kNegInf;
+            for (int64_t i = lane; i < a.nch; i += kWave) mm = fmaxf(mm, load_partial(part + i).x);
+            const float gsh = guarded_shift(wave_reduce<MaxOp>(mm));
+            float ll = 0.0f;
+            for (int64_t i = lane; i < a.nch; i += kWave) {
+                const float2 p = load_partial(part + i);
+                ll += (p.x == kNegInf) ? 0.0f : p.y * exp2_hw((p.x - gsh) * k);
+            }
+            const float gl = wave_reduce<SumOp>(ll);
+            if (lane == 0)
+                chunk_scale = (pm == kNegInf) ? 0.0f : exp2_hw((pm - gsh) * k) * (1.0f / gl);
+        }
+        __syncthreads();
+        const float scale = chunk_scale;
+#pragma unroll
+        for (int i = 0; i < 4 * F; ++i) x[i] *= scale;
+        store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+        __syncthreads();   // chunk_scale is rewritten by the next item
+    }
+}
+
+// ---------------------------------------------------------------------------
+// rowwise, resident: one workgroup of RT lanes holds the whole row (V <= C).
+// ---------------------------------------------------------------------------
+template <int RT, int F, bool VEC>
+__global__ __launch_bounds__(RT) void ts_rowwise_resident(SoftmaxArgs a) {
+    constexpr int RW = RT / kWave;
+    __shared__ float red[RW];
+    const int64_t row = blockIdx.x;
+    const float k = exp2_scale(a.temps[row]);
+    float x[4 * F];
+    load_chunk<RT, F, VEC, true>(a.logits + row * a.V, 0, a.V, x);
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4 * F; ++i) m = fmaxf(m, x[i]);
+    const float gsh = guarded_shift(block_reduce<MaxOp, RW>(m, red));
+    float l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4 * F; ++i) {
+        x[i] = exp2_hw((x[i] - gsh) * k);
+        l += x[i];
+    }
+    const float r = 1.0f / block_reduce<SumOp, RW>(l, red);
+#pragma unroll
+    for (int i = 0; i < 4 * F; ++i) x[i] *= r;
+    store_chunk<RT, F, VEC, true>(a.out + row * a.V, 0, a.V, x);
+}
+
+// ---------------------------------------------------------------------------
+// rowwise, streaming: online (m, l) per lane over the row, a workgroup
+// combine, then a write sweep. Tile = RT lanes x U float4 (or 4U scalars).
+// ---------------------------------------------------------------------------
+template <int RT, bool VEC>
+__global__ __launch_bounds__(RT) void ts_rowwise_stream(SoftmaxArgs a) {
+    constexpr int RW = RT / kWave;
+    constexpr int U = 4;
+    constexpr int TILE = RT * 4 * U;
+    __shared__ float red[RW];
+    const int64_t row = blockIdx.x;
+    const float k = exp2_scale(a.temps[row]);
+    const float* xr = a.logits + row * a.V;
+    float* yr = a.out + row * a.V;
+
+    float m = kNegInf, l = 0.0f;
+    for (int64_t c0 = 0; c0 < a.V; c0 += TILE) {
+        float x[4 * U];
+        load_chunk<RT, U, VEC, false>(xr, c0, a.V, x);
+        float bm = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4 * U; ++i) bm = fmaxf(bm, x[i]);
+        const float nm = fmaxf(m, bm);
+        const float sh = guarded_shift(nm);
+        // m = -inf gives exp2(-inf) = 0 with l = 0; sh is always finite.
+        float s = l * exp2_hw((m - sh) * k);
+#pragma unroll
+        for (int i = 0; i < 4 * U; ++i) s += exp2_hw((x[i] - sh) * k);
+        l = s;
+        m = nm;
+    }
+    const float gsh = guarded_shift(block_reduce<MaxOp, RW>(m, red));
+    const float mine = (m == kNegInf) ? 0.0f : l * exp2_hw((m - gsh) * k);
+    const float r = 1.0f / block_reduce<SumOp, RW>(mine, red);
+    for (int64_t c0 = 0; c0 < a.V; c0 += TILE) {
+        float x[4 * U];
+        load_chunk<RT, U, VEC, true>(xr, c0, a.V, x);
+#pragma unroll
+        for (int i = 0; i < 4 * U; ++i) x[i] = exp2_hw((x[i] - gsh) * k) * r;
+        store_chunk<RT, U, VEC, true>(yr, c0, a.V, x);
+    }
+}
+
+template <int F, bool VEC>
+hipError_t split_impl(const SoftmaxArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(a.items));
+    hipLaunchKernelGGL((ts_split_partials<F, VEC>), grid, dim3(NT), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ts_split_finalize_write<F, VEC>), grid, dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int F, bool VEC>
+hipError_t fused_impl(const SoftmaxArgs& a, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((ts_fused<F, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int F, bool VEC>
+hipError_t fused_cap_impl(int64_t* cap) {
+    int dev = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ts_fused<F, VEC>),
+                                                     NT, 0);
+    if (e != hipSuccess) return e;
+    *cap = static_cast<int64_t>(per_cu) * prop.multiProcessorCount;
+    return hipSuccess;
+}
+
+
+#define TS_DISPATCH_F(IMPL, F, VEC, ...)                                       \
+    do {                                                                       \
+        switch (F) {                                                           \
+            case 1: return VEC ? IMPL<1, true>(__VA_ARGS__) : IMPL<1, false>(__VA_ARGS__);   \
+            case 2: return VEC ? IMPL<2, true>(__VA_ARGS__) : IMPL<2, false>(__VA_ARGS__);   \
+            case 4: return VEC ? IMPL<4, true>(__VA_ARGS__) : IMPL<4, false>(__VA_ARGS__);   \
+            case 8: return VEC ? IMPL<8, true>(__VA_ARGS__) : IMPL<8, false>(__VA_ARGS__);   \
+            case 16: return VEC ? IMPL<16, true>(__VA_ARGS__) : IMPL<16, false>(__VA_ARGS__); \
+            default: return hipErrorInvalidValue;                              \
+        }                                                                      \
+    } while (0)
+
+}  // namespace
+
+hipError_t launch_split(const SoftmaxArgs& a, int F, bool vec, hipStream_t s) {
+    TS_DISPATCH_F(split_impl, F, vec, a, s);
+}
+
+hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int64_t grid, hipStream_t s) {
+    TS_DISPATCH_F(fused_impl, F, vec, a, grid, s);
+}
+
+hipError_t fused_resident_capacity(int F, bool vec, int64_t* cap) {
+    TS_DISPATCH_F(fused_cap_impl, F, vec, cap);
+}
+
+hipError_t launch_rowwise(const SoftmaxArgs& a, bool vec, hipStream_t s) {
+    constexpr int RT = kRowwiseThreads;
+    const dim3 grid(static_cast<uint32_t>(a.B));
+    if (a.V <= RT * 4 * 1) {
+        if (vec) hipLaunchKernelGGL((ts_rowwise_resident<RT, 1, true>), grid, dim3(RT), 0, s, a);
+        else hipLaunchKernelGGL((ts_rowwise_resident<RT, 1, false>), grid, dim3(RT), 0, s, a);
+    } else if (a.V <= RT * 4 * 2) {
+        if (vec) hipLaunchKernelGGL((ts_rowwise_resident<RT, 2, true>), grid, dim3(RT), 0, s, a);
+        else hipLaunchKernelGGL((ts_rowwise_resident<RT, 2, false>), grid, dim3(RT), 0, s, a);
+    } else if (a.V <= kRowwiseResidentMaxV) {
+        if (vec) hipLaunchKernelGGL((ts_rowwise_resident<RT, 4, true>), grid, dim3(RT), 0, s, a);
+        else hipLaunchKernelGGL((ts_rowwise_resident<RT, 4, false>), grid, dim3(RT), 0, s, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((ts_rowwise_stream<RT, true>), grid, dim3(RT), 0, s, a);
+        else hipLaunchKernelGGL((ts_rowwise_stream<RT, false>), grid, dim3(RT), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tsk

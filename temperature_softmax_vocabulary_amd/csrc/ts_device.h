@@ -1,0 +1,151 @@
+// Device-side building blocks shared by the tsoftmax kernels (gfx950, wave64).
+//
+// Notation follows the pull-request page "fix(kernel): avoid nan in triton
+// sampling softmax when a chunk starts with -inf" (FreeToken pull request 654,
+// bug and fix paragraphs): m is a running max, l a sum of exponentials taken
+// relative to it, (pm, pl) a chunk's partial, gm the row's global max.
+//
+// The exponentials are evaluated as exp2((x - shift) * k) with k = log2(e) / T:
+// subtracting the shift in the raw-logit domain keeps the exponent's rounding
+// error proportional to |x - shift|, and exp2 maps to one v_exp_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsk {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_inff();
+constexpr double kLog2eD = 1.4426950408889634073599246810019;
+
+// k = log2(e) / T, formed in double and rounded once to float.
+__device__ __forceinline__ float exp2_scale(float T) {
+    return static_cast<float>(kLog2eD / static_cast<double>(T));
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The fix (fix paragraph): while a max is still -inf the shift is 0, so an all
+// -inf block contributes exp2(-inf) = 0 instead of exp2(-inf - -inf) = NaN.
+// For a finite max this is the plain max: a pure select, no change to the
+// arithmetic of rows without -inf.
+__device__ __forceinline__ float guarded_shift(float m) { return m == kNegInf ? 0.0f : m; }
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions with DPP. Steps: two quad permutes (sum of 4 lanes), half
+// row mirror (8), row mirror (16), then row_bcast15 and row_bcast31 fold the
+// four rows of 16 into lane 63, which readlane returns to every lane.
+// Must be called with all 64 lanes active.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_or(float v, float fill) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL,
+                                                      ROW_MASK, 0xF, false));
+}
+
+struct MaxOp {
+    static constexpr float identity = kNegInf;
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct SumOp {
+    static constexpr float identity = 0.0f;
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v) {
+    Op op;
+    v = op(v, dpp_or<0xB1>(v, Op::identity));          // quad_perm [1,0,3,2]
+    v = op(v, dpp_or<0x4E>(v, Op::identity));          // quad_perm [2,3,0,1]
+    v = op(v, dpp_or<0x141>(v, Op::identity));         // row_half_mirror
+    v = op(v, dpp_or<0x140>(v, Op::identity));         // row_mirror
+    v = op(v, dpp_or<0x142, 0xA>(v, Op::identity));    // row_bcast15 -> rows 1, 3
+    v = op(v, dpp_or<0x143, 0xC>(v, Op::identity));    // row_bcast31 -> rows 2, 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Workgroup reduction: wave64 DPP reduce, then a fixed-order combine of the
+// NW wave results through LDS. The order never depends on timing, so results
+// are bitwise reproducible. `lds` holds NW floats; the trailing barrier lets
+// the caller reuse it immediately.
+template <class Op, int NW>
+__device__ __forceinline__ float block_reduce(float v, float* lds) {
+    v = wave_reduce<Op>(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = v;
+    __syncthreads();
+    Op op;
+    float r = lds[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) r = op(r, lds[i]);
+    __syncthreads();
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk access. A chunk is C = NT * 4 * F consecutive columns of one row.
+// Vector path (16-byte aligned row, V % 4 == 0): lane t of the workgroup owns
+// the float4 at column c0 + (j * NT + t) * 4 for j in [0, F), so each wave64
+// load instruction covers 1 KiB of contiguous memory. Scalar path: lane t owns
+// columns c0 + j * NT + t for j in [0, 4F). Columns at or past V read as -inf.
+// ---------------------------------------------------------------------------
+template <int NT, int F, bool VEC, bool NT_LOAD>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t c0, int64_t V,
+                                           float (&x)[4 * F]) {
+    const int t = threadIdx.x;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+            f4 v = {kNegInf, kNegInf, kNegInf, kNegInf};
+            if (col < V) {
+                const f4* p = reinterpret_cast<const f4*>(row + col);
+                if constexpr (NT_LOAD) v = __builtin_nontemporal_load(p);
+                else v = *p;
+            }
+            x[4 * j + 0] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4 * F; ++j) {
+            const int64_t col = c0 + static_cast<int64_t>(j) * NT + t;
+            float v = kNegInf;
+            if (col < V) {
+                if constexpr (NT_LOAD) v = __builtin_nontemporal_load(row + col);
+                else v = row[col];
+            }
+            x[j] = v;
+        }
+    }
+}
+
+template <int NT, int F, bool VEC, bool NT_STORE>
+__device__ __forceinline__ void store_chunk(float* __restrict__ row, int64_t c0, int64_t V,
+                                            const float (&y)[4 * F]) {
+    const int t = threadIdx.x;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+            if (col < V) {
+                f4 v = {y[4 * j + 0], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]};
+                f4* p = reinterpret_cast<f4*>(row + col);
+                if constexpr (NT_STORE) __builtin_nontemporal_store(v, p);
+                else *p = v;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4 * F; ++j) {
+            const int64_t col = c0 + static_cast<int64_t>(j) * NT + t;
+            if (col < V) {
+                if constexpr (NT_STORE) __builtin_nontemporal_store(y[j], row + col);
+                else row[col] = y[j];
+            }
+        }
+    }
+}
+
+}  // namespace tsk

@@ -1,0 +1,53 @@
+// Internal host-side launch interface between the C-ABI layer and the HIP
+// kernels. Not installed, not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsk {
+
+// Columns per chunk for the split and fused kernels: 1024 * F, F in {1,2,4,8,16}
+// (256 lanes x F float4 each).
+constexpr int kChunkThreads = 256;
+constexpr int kMinChunk = 1024;
+constexpr int kMaxChunk = 16384;
+
+// Largest row the resident one-workgroup-per-row kernel holds in registers.
+constexpr int kRowwiseThreads = 1024;
+constexpr int64_t kRowwiseResidentMaxV = 16384;
+
+struct SoftmaxArgs {
+    const float* logits;   // [B, V]
+    const float* temps;    // [B]
+    float* out;            // [B, V]
+    int64_t B;
+    int64_t V;
+    int64_t nch;           // chunks per row (split, fused)
+    int64_t items;         // B * nch
+    float2* part;          // [B * nch] chunk partials (pm, pl)
+    uint32_t* cnt;         // [B] per-row arrival counters (fused), zero between calls
+    uint32_t* gen;         // [B] per-row generation words (fused)
+    uint32_t* err;         // device error flags (bit 0: a bounded wait ran out)
+    uint32_t spin_limit;   // polls before a fused wait gives up
+};
+
+hipError_t launch_split(const SoftmaxArgs& a, int F, bool vec, hipStream_t s);
+hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int64_t grid, hipStream_t s);
+// Workgroups of the fused kernel that one device holds at once (occupancy x CUs).
+hipError_t fused_resident_capacity(int F, bool vec, int64_t* cap);
+hipError_t launch_rowwise(const SoftmaxArgs& a, bool vec, hipStream_t s);
+
+struct SampleArgs {
+    const float* probs;      // [B, V]
+    const float* uniforms;   // [B, K]
+    int32_t* out_ids;        // [B, K]
+    int64_t B;
+    int64_t V;
+    int64_t K;
+};
+hipError_t launch_sample(const SampleArgs& a, bool vec, hipStream_t s);
+
+hipError_t launch_copy(const float* src, float* dst, int64_t n, bool vec, hipStream_t s);
+
+}  // namespace tsk

@@ -1,0 +1,347 @@
+// C-ABI layer of libtsoftmax: argument checks, the (B, V) -> work-split table,
+// the per-stream workspace, and kernel dispatch. Host code only; every step of
+// the computation runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/tsoftmax.h"
+#include "../../include/tsoftmax_measure.h"
+#include "ts_launch.h"
+
+#define TS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr uint32_t kDefaultSpinLimit = 1u << 18;
+std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
+
+// ----------------------------------------------------------------------------
+// argument checks (host only: no device reads)
+// ----------------------------------------------------------------------------
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// B * V * 4 bytes must be addressable and the element count must fit int64.
+bool sizes_ok(int64_t B, int64_t V) {
+    if (B < 0 || V < 1 || V > INT32_MAX) return false;
+    return B <= (INT64_MAX / 8) / V;
+}
+
+// ----------------------------------------------------------------------------
+// workspace: one per (device, stream), grow-only, zeroed when allocated.
+// Layout is fixed by the allocation's capacity, never by the call, so the
+// fused kernel's counters stay at the same addresses (and at zero between
+// calls) whatever B the calls use:
+//   [0, 256)                 flags (uint32 at offset 0)
+//   [256, 256 + 4 Bcap)      cnt[Bcap]
+//   [.., + 4 Bcap)           gen[Bcap]
+//   [aligned 256, + 8 Pcap)  part[Pcap] (float2)
+// ----------------------------------------------------------------------------
+struct Workspace {
+    void* base = nullptr;
+    int64_t bcap = 0;   // rows
+    int64_t pcap = 0;   // partials
+};
+
+struct WsView {
+    uint32_t* err;
+    uint32_t* cnt;
+    uint32_t* gen;
+    float2* part;
+};
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+int64_t ws_bytes(int64_t bcap, int64_t pcap) {
+    return align256(256 + 8 * bcap) + 8 * pcap;
+}
+
+WsView ws_view(const Workspace& w) {
+    char* b = static_cast<char*>(w.base);
+    WsView v;
+    v.err = reinterpret_cast<uint32_t*>(b);
+    v.cnt = reinterpret_cast<uint32_t*>(b + 256);
+    v.gen = reinterpret_cast<uint32_t*>(b + 256 + 4 * w.bcap);
+    v.part = reinterpret_cast<float2*>(b + align256(256 + 8 * w.bcap));
+    return v;
+}
+
+std::mutex g_mu;   // guards g_ws and is held across each launch that uses it
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+ts_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return TS_OK;
+    if (e == hipErrorOutOfMemory) return TS_ERR_OUT_OF_MEMORY;
+    return TS_ERR_HIP;
+}
+
+// Called with g_mu held. Makes the stream's workspace hold >= need_b rows and
+// need_p partials, allocating (outside capture only) and zeroing if it grows.
+ts_status ws_get(hipStream_t stream, int64_t need_b, int64_t need_p, Workspace** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return TS_ERR_HIP;
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.base && w.bcap >= need_b && w.pcap >= need_p) {
+        *out = &w;
+        return TS_OK;
+    }
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return TS_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return TS_ERR_NOT_RESERVED;
+    const int64_t nb = need_b > w.bcap ? need_b : w.bcap;
+    const int64_t np = need_p > w.pcap ? need_p : w.pcap;
+    if (w.base) {
+        // Work already queued on this stream may still use the old buffer.
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return TS_ERR_HIP;
+        (void)hipFree(w.base);
+        w = Workspace{};
+    }
+    void* p = nullptr;
+    const int64_t bytes = ws_bytes(nb, np);
+    e = hipMalloc(&p, static_cast<size_t>(bytes));
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? TS_ERR_OUT_OF_MEMORY : TS_ERR_HIP;
+    e = hipMemsetAsync(p, 0, static_cast<size_t>(bytes), stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return TS_ERR_HIP;
+    }
+    w.base = p;
+    w.bcap = nb;
+    w.pcap = np;
+    *out = &w;
+    return TS_OK;
+}
+
+// ----------------------------------------------------------------------------
+// work-split table (a7): variant and chunk from (B, V)
+// ----------------------------------------------------------------------------
+constexpr int kFs[] = {1, 2, 4, 8, 16};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+    int variant;
+    int F;   // chunk = 1024 * F (split, fused)
+};
+
+// Fused-kernel residency per F on the current device (cached per device).
+ts_status fused_caps(bool vec, int64_t caps[5]) {
+    static std::mutex mu;
+    static std::map<std::pair<int, bool>, std::array<int64_t, 5>> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TS_ERR_HIP;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find({dev, vec});
+    if (it == cache.end()) {
+        std::array<int64_t, 5> c{};
+        for (int i = 0; i < 5; ++i)
+            if (tsk::fused_resident_capacity(kFs[i], vec, &c[i]) != hipSuccess) return TS_ERR_HIP;
+        it = cache.emplace(std::make_pair(dev, vec), c).first;
+    }
+    for (int i = 0; i < 5; ++i) caps[i] = it->second[i];
+    return TS_OK;
+}
+
+// Rows that fit one workgroup's registers go one workgroup per row (single
+// read, no partials). Longer rows go to the fused kernel with the smallest
+// chunk whose grid fits the device at once; if no chunk size fits, the one
+// with the fewest items runs persistent (each workgroup loops over items).
+ts_status choose_plan(int64_t B, int64_t V, bool vec, Plan* p) {
+    if (V <= tsk::kRowwiseResidentMaxV) {
+        *p = Plan{TS_VARIANT_ROWWISE, 0};
+        return TS_OK;
+    }
+    int64_t caps[5];
+    ts_status st = fused_caps(vec, caps);
+    if (st != TS_OK) return st;
+    for (int i = 0; i < 5; ++i) {
+        if (B * cdiv(V, 1024 * kFs[i]) <= caps[i]) {
+            *p = Plan{TS_VARIANT_FUSED, kFs[i]};
+            return TS_OK;
+        }
+    }
+    if (cdiv(V, 1024 * 16) <= caps[4]) {
+        *p = Plan{TS_VARIANT_FUSED, 16};
+        return TS_OK;
+    }
+    *p = Plan{TS_VARIANT_SPLIT, 16};
+    return TS_OK;
+}
+
+ts_status run_softmax(const float* logits, const float* temps, int64_t B, int64_t V, float* out,
+                      int variant, int chunk, hipStream_t stream) {
+    if (!sizes_ok(B, V)) return TS_ERR_INVALID_ARGUMENT;
+    if (B == 0) return TS_OK;
+    if (!logits || !temps || !out) return TS_ERR_INVALID_ARGUMENT;
+    const int64_t xbytes = B * V * 4;
+    if (out != logits && overlaps(out, xbytes, logits, xbytes)) return TS_ERR_INVALID_ARGUMENT;
+    if (overlaps(out, xbytes, temps, B * 4)) return TS_ERR_INVALID_ARGUMENT;
+    if (variant < TS_VARIANT_AUTO || variant > TS_VARIANT_FUSED) return TS_ERR_INVALID_ARGUMENT;
+    int F = 0;
+    if (chunk != 0) {
+        if (chunk % 1024 != 0) return TS_ERR_INVALID_ARGUMENT;
+        F = chunk / 1024;
+        if (F != 1 && F != 2 && F != 4 && F != 8 && F != 16) return TS_ERR_INVALID_ARGUMENT;
+    }
+    const bool vec = aligned16(logits) && aligned16(out) && (V % 4 == 0);
+
+    Plan plan{variant, F};
+    if (variant == TS_VARIANT_AUTO) {
+        ts_status st = choose_plan(B, V, vec, &plan);
+        if (st != TS_OK) return st;
+        if (F != 0 && plan.variant != TS_VARIANT_ROWWISE) plan.F = F;
+    }
+    if (plan.variant != TS_VARIANT_ROWWISE && plan.F == 0) {
+        // the smallest chunk giving at least ~2 workgroups per CU, else 16K
+        plan.F = 16;
+        for (int f : kFs) {
+            if (B * cdiv(V, 1024 * f) <= 2048) { plan.F = f; break; }
+        }
+    }
+
+    tsk::SoftmaxArgs a{};
+    a.logits = logits;
+    a.temps = temps;
+    a.out = out;
+    a.B = B;
+    a.V = V;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+
+    if (plan.variant == TS_VARIANT_ROWWISE) {
+        if (B > INT32_MAX) return TS_ERR_INVALID_ARGUMENT;
+        return hip_status(tsk::launch_rowwise(a, vec, stream));
+    }
+
+    a.nch = cdiv(V, 1024 * plan.F);
+    a.items = B * a.nch;
+    int64_t grid = a.items;
+    if (plan.variant == TS_VARIANT_FUSED) {
+        int64_t caps[5];
+        ts_status st = fused_caps(vec, caps);
+        if (st != TS_OK) return st;
+        int fi = 0;
+        while (kFs[fi] != plan.F) ++fi;
+        // The lowest unfinished row must fit the device at once (see ts_fused).
+        if (a.nch > caps[fi] || caps[fi] < 1) return TS_ERR_INVALID_ARGUMENT;
+        if (grid > caps[fi]) grid = caps[fi];
+    } else if (a.items > INT32_MAX) {
+        return TS_ERR_INVALID_ARGUMENT;
+    }
+
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace* w = nullptr;
+    ts_status st = ws_get(stream, plan.variant == TS_VARIANT_FUSED ? B : 0, a.items, &w);
+    if (st != TS_OK) return st;
+    const WsView v = ws_view(*w);
+    a.part = v.part;
+    a.cnt = v.cnt;
+    a.gen = v.gen;
+    a.err = v.err;
+    if (plan.variant == TS_VARIANT_FUSED) return hip_status(tsk::launch_fused(a, plan.F, vec, grid, stream));
+    return hip_status(tsk::launch_split(a, plan.F, vec, stream));
+}
+
+}  // namespace
+
+TS_API ts_status ts_softmax(const float* logits, const float* temps, int64_t B, int64_t V, float* out,
+                            hipStream_t stream) {
+    return run_softmax(logits, temps, B, V, out, TS_VARIANT_AUTO, 0, stream);
+}
+
+TS_API ts_status ts_softmax_variant(const float* logits, const float* temps, int64_t B, int64_t V,
+                                    float* out, int32_t variant, int32_t chunk, hipStream_t stream) {
+    return run_softmax(logits, temps, B, V, out, variant, chunk, stream);
+}
+
+TS_API ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk) {
+    if (!sizes_ok(B, V) || !variant || !chunk) return TS_ERR_INVALID_ARGUMENT;
+    Plan p{};
+    ts_status st = choose_plan(B, V, true, &p);
+    if (st != TS_OK) return st;
+    *variant = p.variant;
+    *chunk = p.F * 1024;
+    return TS_OK;
+}
+
+TS_API ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_t V, int64_t K,
+                           int32_t* out_ids, hipStream_t stream) {
+    if (!sizes_ok(B, V) || K < 0 || (K > 0 && B > (INT64_MAX / 8) / K)) return TS_ERR_INVALID_ARGUMENT;
+    if (B == 0 || K == 0) return TS_OK;
+    if (!probs || !uniforms || !out_ids) return TS_ERR_INVALID_ARGUMENT;
+    if (B > INT32_MAX) return TS_ERR_INVALID_ARGUMENT;
+    if (overlaps(out_ids, B * K * 4, probs, B * V * 4) || overlaps(out_ids, B * K * 4, uniforms, B * K * 4))
+        return TS_ERR_INVALID_ARGUMENT;
+    tsk::SampleArgs a{probs, uniforms, out_ids, B, V, K};
+    const bool vec = aligned16(probs) && (V % 4 == 0);
+    return hip_status(tsk::launch_sample(a, vec, stream));
+}
+
+TS_API ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream) {
+    if (!sizes_ok(max_B, max_V)) return TS_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace* w = nullptr;
+    return ws_get(stream, max_B, max_B * cdiv(max_V, tsk::kMinChunk), &w);
+}
+
+TS_API ts_status ts_device_errors(hipStream_t stream, uint32_t* flags) {
+    if (!flags) return TS_ERR_INVALID_ARGUMENT;
+    *flags = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TS_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || !it->second.base) return TS_OK;
+    if (hipStreamSynchronize(stream) != hipSuccess) return TS_ERR_HIP;
+    uint32_t f = 0;
+    if (hipMemcpy(&f, it->second.base, 4, hipMemcpyDeviceToHost) != hipSuccess) return TS_ERR_HIP;
+    if (f != 0) {
+        // A timed-out wait may leave a row's counter short of zero: clear all.
+        const int64_t bytes = ws_bytes(it->second.bcap, it->second.pcap);
+        if (hipMemset(it->second.base, 0, static_cast<size_t>(bytes)) != hipSuccess) return TS_ERR_HIP;
+    }
+    *flags = f;
+    return (f & 1u) ? TS_ERR_SYNC_TIMEOUT : TS_OK;
+}
+
+TS_API const char* ts_status_string(ts_status s) {
+    switch (s) {
+        case TS_OK: return "TS_OK";
+        case TS_ERR_INVALID_ARGUMENT: return "TS_ERR_INVALID_ARGUMENT: a pointer, size or alias rule was broken";
+        case TS_ERR_HIP: return "TS_ERR_HIP: the HIP runtime reported an error";
+        case TS_ERR_OUT_OF_MEMORY: return "TS_ERR_OUT_OF_MEMORY: workspace allocation failed";
+        case TS_ERR_NOT_RESERVED:
+            return "TS_ERR_NOT_RESERVED: the stream is capturing and the workspace is too small; call ts_reserve first";
+        case TS_ERR_SYNC_TIMEOUT: return "TS_ERR_SYNC_TIMEOUT: a fused kernel's bounded wait ran out";
+    }
+    return "unknown ts_status";
+}
+
+TS_API int32_t ts_abi_version(void) { return TSOFTMAX_ABI_VERSION; }
+
+TS_API ts_status ts_copy_f32(const float* src, float* dst, int64_t n, hipStream_t stream) {
+    if (n < 0 || n > INT64_MAX / 8) return TS_ERR_INVALID_ARGUMENT;
+    if (n == 0) return TS_OK;
+    if (!src || !dst || overlaps(src, n * 4, dst, n * 4)) return TS_ERR_INVALID_ARGUMENT;
+    const bool vec = aligned16(src) && aligned16(dst);
+    return hip_status(tsk::launch_copy(src, dst, n, vec, stream));
+}
+
+TS_API ts_status ts_debug_set_spin_limit(uint32_t polls) {
+    g_spin_limit.store(polls == 0 ? kDefaultSpinLimit : polls, std::memory_order_relaxed);
+    return TS_OK;
+}

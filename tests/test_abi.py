@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every function include/*.h declares, and
+its host-side argument checks reject bad calls before any HIP work. Runs
+without a GPU: every call here returns before the library touches a device."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import temperature_softmax_vocabulary_amd as tsv
+from temperature_softmax_vocabulary_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_A = 0x10000000       # never dereferenced: checks fail before any device access
+FAKE_B = 0x20000000
+INVALID = binding.TS_ERR_INVALID_ARGUMENT
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(ts_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail(f"{binding.LIB_PATH} missing: build it with python -m temperature_softmax_vocabulary_amd.build")
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = _declared_functions()
+    assert {"ts_softmax", "ts_sample", "ts_reserve", "ts_status_string"} <= declared
+    for name in sorted(declared):
+        assert hasattr(L, name), f"{name} declared in include/ but not exported"
+    # and the binding wraps exactly the declared set
+    assert set(binding.SIGNATURES) == declared
+
+
+def test_abi_version_and_status_strings(L):
+    assert tsv.ts_abi_version() == 1
+    for s in range(6):
+        assert tsv.ts_status_string(s).startswith("TS_")
+    assert "unknown" in tsv.ts_status_string(99)
+
+
+@pytest.mark.parametrize("B,V", [(-1, 10), (1, 0), (1, -5), (1, 2**31), (2**40, 2**31 - 1)])
+def test_softmax_rejects_bad_sizes(L, B, V):
+    assert L.ts_softmax(FAKE_A, FAKE_B, B, V, FAKE_A + (1 << 40), None) == INVALID
+
+
+def test_softmax_zero_rows_is_a_noop(L):
+    assert L.ts_softmax(None, None, 0, 151936, None, None) == binding.TS_OK
+
+
+def test_softmax_rejects_null_pointers(L):
+    assert L.ts_softmax(None, FAKE_B, 3, 100, FAKE_A, None) == INVALID
+    assert L.ts_softmax(FAKE_A, None, 3, 100, FAKE_A, None) == INVALID
+    assert L.ts_softmax(FAKE_A, FAKE_B, 3, 100, None, None) == INVALID
+
+
+def test_softmax_rejects_partial_overlap_but_not_exact_alias_check(L):
+    # out shifted by one float inside logits: rejected
+    assert L.ts_softmax(FAKE_A, FAKE_B, 2, 100, FAKE_A + 4, None) == INVALID
+    # out overlapping temps: rejected
+    assert L.ts_softmax(FAKE_A, FAKE_B + 8, 2, 100, FAKE_B, None) == INVALID
+
+
+def test_softmax_variant_rejects_bad_variant_or_chunk(L):
+    assert L.ts_softmax_variant(FAKE_A, FAKE_B, 2, 100, FAKE_A, 7, 0, None) == INVALID
+    assert L.ts_softmax_variant(FAKE_A, FAKE_B, 2, 100, FAKE_A, 1, 3000, None) == INVALID
+    assert L.ts_softmax_variant(FAKE_A, FAKE_B, 2, 100, FAKE_A, 1, 32768, None) == INVALID
+
+
+def test_sample_argument_checks(L):
+    assert L.ts_sample(FAKE_A, FAKE_B, 1, 10, -1, FAKE_A + (1 << 30), None) == INVALID
+    assert L.ts_sample(None, FAKE_B, 1, 10, 4, FAKE_A, None) == INVALID
+    assert L.ts_sample(FAKE_A, FAKE_B, 0, 10, 4, None, None) == binding.TS_OK
+    assert L.ts_sample(FAKE_A, FAKE_B, 2, 10, 0, None, None) == binding.TS_OK
+    # ids written over the probs: rejected
+    assert L.ts_sample(FAKE_A, FAKE_B, 2, 10, 4, FAKE_A + 16, None) == INVALID
+    assert L.ts_sample(FAKE_A, FAKE_B, 2, 10, 4, FAKE_B + 4, None) == INVALID
+
+
+def test_reserve_plan_copy_argument_checks(L):
+    assert L.ts_reserve(-1, 10, None) == INVALID
+    assert L.ts_reserve(1, 0, None) == INVALID
+    v = ctypes.c_int32()
+    assert L.ts_plan(1, 10, None, ctypes.byref(v)) == INVALID
+    assert L.ts_plan(-1, 10, ctypes.byref(v), ctypes.byref(v)) == INVALID
+    assert L.ts_copy_f32(FAKE_A, FAKE_A + 8, 100, None) == INVALID
+    assert L.ts_copy_f32(FAKE_A, FAKE_B, -1, None) == INVALID
+    assert L.ts_copy_f32(None, None, 0, None) == binding.TS_OK
+    assert L.ts_device_errors(None, None) == INVALID
+    assert L.ts_debug_set_spin_limit(0) == binding.TS_OK
+
+
+def test_binding_raises_value_error_on_invalid_argument():
+    with pytest.raises(ValueError):
+        binding._check(INVALID)
+    with pytest.raises(binding.TsError):
+        binding._check(binding.TS_ERR_HIP)
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    # The package never imports the oracle, and nothing under it names a CPU
+    # softmax route: the binding only marshals arguments into the library.
+    pkg = os.path.join(ROOT, "temperature_softmax_vocabulary_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*.py"), recursive=True):
+        text = open(path).read()
+        assert "oracle" not in text.replace("oracle's", ""), path
+        assert "torch.softmax" not in text and "np.exp" not in text, path

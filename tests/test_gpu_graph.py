@@ -1,0 +1,69 @@
+"""HIP-graph capture of ts_softmax and ts_sample, replayed with fresh inputs.
+
+Pattern: capture once into static buffers, then several replays, each with new
+inputs copied in and checked against the oracle, with eager work and
+synchronisations between the replays. The workspace is reserved before the
+capture so that the captured calls allocate nothing.
+"""
+import numpy as np
+import pytest
+import torch
+
+import temperature_softmax_vocabulary_amd as tsv
+from oracle import softmax_ref
+from temperature_softmax_vocabulary_amd import workloads
+from tests.parity import assert_ids_valid, assert_softmax_matches
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("variant,chunk", [(tsv.TS_VARIANT_AUTO, 0), (tsv.TS_VARIANT_SPLIT, 4096),
+                                           (tsv.TS_VARIANT_FUSED, 8192), (tsv.TS_VARIANT_ROWWISE, 0)])
+def test_capture_and_replay_softmax_then_sample(variant, chunk):
+    B, V, K = 16, 201088, 64
+    s = torch.cuda.Stream(device=DEV)
+    tsv.ts_reserve(B, V, device=DEV, stream=s)
+    x = torch.zeros((B, V), dtype=torch.float32, device=DEV)
+    t = torch.ones((B,), dtype=torch.float32, device=DEV)
+    u = torch.zeros((B, K), dtype=torch.float32, device=DEV)
+    y = torch.empty_like(x)
+    ids = torch.empty((B, K), dtype=torch.int32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        # warm-up on the capture stream, outside capture
+        tsv.ts_softmax_variant(x, t, variant, chunk, out=y) if variant else tsv.ts_softmax(x, t, out=y)
+        tsv.ts_sample(y, u, out_ids=ids)
+    s.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        if variant:
+            tsv.ts_softmax_variant(x, t, variant, chunk, out=y)
+        else:
+            tsv.ts_softmax(x, t, out=y)
+        tsv.ts_sample(y, u, out_ids=ids)
+    for rep in range(3):
+        w = workloads.make(B, V, "quarters", K=K, seed=1000 + rep)
+        x.copy_(torch.from_numpy(w.logits))
+        t.copy_(torch.from_numpy(w.temps))
+        u.copy_(torch.from_numpy(w.uniforms))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert_softmax_matches(got, w.logits, w.temps, what=f"replay {rep}")
+        assert_ids_valid(ids.cpu().numpy(), got, w.uniforms, what=f"replay {rep}")
+        # eager work between replays
+        _ = (x * 2).sum().item()
+    assert tsv.ts_device_errors(device=DEV, stream=s) == 0
+
+
+def test_capture_without_reserve_is_refused():
+    B, V = 8, 300000
+    s = torch.cuda.Stream(device=DEV)
+    x = torch.zeros((B, V), dtype=torch.float32, device=DEV)
+    t = torch.ones((B,), dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(tsv.TsError) as ei:
+        with torch.cuda.graph(g, stream=s):
+            tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, 1024)
+    assert ei.value.status == tsv.TS_ERR_NOT_RESERVED
