@@ -98,25 +98,44 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fused: one read of the logits.
+// fused: one read of the logits, one kernel.
 //
-// Workgroup w handles items w, w + gridDim.x, ... (item = row * nch + chunk).
-// The host launches at most as many workgroups as the device holds at once and
-// at least nch of them, so every chunk of the lowest unfinished row is always
-// either done or resident and waiting: the row completes and no wait can
-// deadlock. Each wait is still bounded (spin_limit polls); running out raises
-// bit 0 of *err instead of hanging.
+// Work items are (row, chunk) pairs, item = row * nch + chunk. Workgroup w
+// handles items w, w + gridDim.x, ... in order, and issues the loads of its
+// next item before it waits on the current row, so a workgroup's wait and
+// stores overlap its next reads. The host launches no more workgroups than the
+// device holds at once and at least nch of them: every chunk of the lowest
+// unfinished row is then done or resident, so the row always completes. Each
+// wait is still bounded (spin_limit polls; running out raises bit 0 of *err).
 //
-// Exchange per row (agent scope, so it holds across the XCDs' separate L2s):
-//  lane 0 stores (pm, pl), reads gen[row], then increments cnt[row] with
-//  acq_rel. The workgroup that brings cnt to nch resets it to 0 and bumps
-//  gen[row] with release. Every lane of wave 0 then polls gen[row] with
-//  acquire until it differs from the value read before arriving, which orders
-//  all of the row's partial stores before wave 0's reads of them. The counter
-//  is back at 0 when the kernel ends, so the next launch needs no clearing.
+// Exchange of chunk partials, with no fence and no contended read-modify-write
+// (both cost microseconds per workgroup on a multi-XCD part): each row owns
+// kSlotStride 64-bit slots. A slot holds (pm, pl) of one chunk and, in pl's
+// sign bit (pl >= 0, so the bit is free), a parity tag. Between calls every
+// slot of a row carries the same tag t. In a call, the workgroup of chunk c
+// reads its own slot (it is the slot's only writer in the call, so it reads
+// t), stores (pm, pl, t ^ 1) with one 64-bit atomic store, and also stores tag
+// t ^ 1 into the row's unused slots c + nch, c + 2 nch, ... Readers poll the
+// row's nch slots with 64-bit atomic loads until each shows t ^ 1; the value
+// that shows the new tag is the data itself. Only per-location coherence of
+// relaxed agent-scope atomics is used, plus the ordering between launches on
+// a stream. After the call every slot of the row carries t ^ 1 again, whatever
+// nch the next call uses.
 // ---------------------------------------------------------------------------
 template <int F>
-struct FusedOcc { static constexpr int waves_per_eu = F <= 8 ? 8 : 4; };
+struct FusedOcc {
+    // registers hold the current and the next chunk: 8 F floats per lane
+    static constexpr int waves_per_eu = F <= 4 ? 8 : (F == 8 ? 4 : 2);
+};
+
+constexpr unsigned long long kTagBit = 1ull << 63;
+
+__device__ __forceinline__ unsigned long long slot_load(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_store(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int F, bool VEC>
 __global__ __launch_bounds__(NT, FusedOcc<F>::waves_per_eu) void ts_fused(SoftmaxArgs a) {
@@ -124,15 +143,23 @@ __global__ __launch_bounds__(NT, FusedOcc<F>::waves_per_eu) void ts_fused(Softma
     __shared__ float chunk_scale;
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
+    int64_t item = blockIdx.x;
+    if (item >= a.items) return;
 
-    for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+    float x[4 * F], nx[4 * F];
+    unsigned long long own = 0, next_own = 0;   // lane 0: old value of the item's own slot
+    {
+        const int64_t row = item / a.nch, c = item - row * a.nch;
+        load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x);
+        if (lane == 0) own = slot_load(a.slots + row * kSlotStride + c);
+    }
+    for (; item < a.items; item += gridDim.x) {
         const int64_t row = item / a.nch;
         const int64_t c = item - row * a.nch;
         const float k = exp2_scale(a.temps[row]);
+        unsigned long long* rs = a.slots + row * kSlotStride;
 
-        float x[4 * F];
-        load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x);
-
+        // chunk partial: pm = max, pl = sum exp2((x - shift) k); x keeps the exponentials
         float m = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4 * F; ++i) m = fmaxf(m, x[i]);
@@ -141,53 +168,69 @@ __global__ __launch_bounds__(NT, FusedOcc<F>::waves_per_eu) void ts_fused(Softma
         float l = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4 * F; ++i) {
-            x[i] = exp2_hw((x[i] - sh) * k);      // kept: the probs are x[i] * scale
+            x[i] = exp2_hw((x[i] - sh) * k);
             l += x[i];
         }
         const float pl = block_reduce<SumOp, NW>(l, red);
 
+        // publish with the flipped tag
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(own >> 32));
+        const unsigned long long tag = static_cast<unsigned long long>((hi >> 31) ^ 1u) << 63;
+        if (lane == 0)
+            slot_store(rs + c, tag | (static_cast<unsigned long long>(__float_as_uint(pl)) << 32) | __float_as_uint(pm));
+        if (lane < kWave)
+            for (int64_t j = c + a.nch * (1 + lane); j < kSlotStride; j += a.nch * kWave) slot_store(rs + j, tag);
+
+        // prefetch the next item (a later row: gridDim.x >= nch)
+        const int64_t nitem = item + gridDim.x;
+        if (nitem < a.items) {
+            const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
+            load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx);
+            if (lane == 0) next_own = slot_load(a.slots + nr * kSlotStride + nc);
+        }
+
+        // wave 0 waits for the row's slots and combines them (nch <= kSlotStride,
+        // so each lane holds at most kSlotStride / 64 slot values)
         if (lane < kWave) {
-            uint32_t* cnt = a.cnt + row;
-            uint32_t* gen = a.gen + row;
-            uint32_t g0 = 0;
-            if (lane == 0) {
-                a.part[item] = make_float2(pm, pl);
-                g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t before =
-                    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-                if (before + 1 == static_cast<uint32_t>(a.nch)) {
-                    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-            g0 = __builtin_amdgcn_readfirstlane(g0);
-            uint32_t polls = 0;
-            while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
-                if (++polls > a.spin_limit) {
-                    if (lane == 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-            // Wave 0 combines the row's partials (nch <= the resident grid).
-            const float2* part = a.part + row * a.nch;
+            constexpr int SPL = kSlotStride / kWave;
+            float vm[SPL], vl[SPL];
             float mm = kNegInf;
-            for (int64_t i = lane; i < a.nch; i += kWave) mm = fmaxf(mm, load_partial(part + i).x);
+            uint32_t polls = 0;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t i = lane + static_cast<int64_t>(j) * kWave;
+                vm[j] = kNegInf;
+                vl[j] = 0.0f;
+                if (i < a.nch) {
+                    unsigned long long v = slot_load(rs + i);
+                    while ((v & kTagBit) != tag) {
+                        if (++polls > a.spin_limit) {
+                            __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                        v = slot_load(rs + i);
+                    }
+                    vm[j] = __uint_as_float(static_cast<uint32_t>(v));
+                    vl[j] = __uint_as_float(static_cast<uint32_t>(v >> 32) & 0x7fffffffu);
+                    mm = fmaxf(mm, vm[j]);
+                }
+            }
             const float gsh = guarded_shift(wave_reduce<MaxOp>(mm));
             float ll = 0.0f;
-            for (int64_t i = lane; i < a.nch; i += kWave) {
-                const float2 p = load_partial(part + i);
-                ll += (p.x == kNegInf) ? 0.0f : p.y * exp2_hw((p.x - gsh) * k);
-            }
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) ll += (vm[j] == kNegInf) ? 0.0f : vl[j] * exp2_hw((vm[j] - gsh) * k);
             const float gl = wave_reduce<SumOp>(ll);
-            if (lane == 0)
-                chunk_scale = (pm == kNegInf) ? 0.0f : exp2_hw((pm - gsh) * k) * (1.0f / gl);
+            if (lane == 0) chunk_scale = (pm == kNegInf) ? 0.0f : exp2_hw((pm - gsh) * k) * (1.0f / gl);
         }
         __syncthreads();
         const float scale = chunk_scale;
 #pragma unroll
         for (int i = 0; i < 4 * F; ++i) x[i] *= scale;
         store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+#pragma unroll
+        for (int i = 0; i < 4 * F; ++i) x[i] = nx[i];
+        own = next_own;
         __syncthreads();   // chunk_scale is rewritten by the next item
     }
 }

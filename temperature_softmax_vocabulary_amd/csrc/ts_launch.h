@@ -13,6 +13,10 @@ constexpr int kChunkThreads = 256;
 constexpr int kMinChunk = 1024;
 constexpr int kMaxChunk = 16384;
 
+// Slots per row for the fused kernel's partial exchange: it runs only when a
+// row has at most this many chunks.
+constexpr int64_t kSlotStride = 256;
+
 // Largest row the resident one-workgroup-per-row kernel holds in registers.
 constexpr int kRowwiseThreads = 1024;
 constexpr int64_t kRowwiseResidentMaxV = 16384;
@@ -25,9 +29,8 @@ struct SoftmaxArgs {
     int64_t V;
     int64_t nch;           // chunks per row (split, fused)
     int64_t items;         // B * nch
-    float2* part;          // [B * nch] chunk partials (pm, pl)
-    uint32_t* cnt;         // [B] per-row arrival counters (fused), zero between calls
-    uint32_t* gen;         // [B] per-row generation words (fused)
+    float2* part;          // [B * nch] chunk partials (pm, pl) of the split kernels
+    unsigned long long* slots;  // [B * kSlotStride] tagged partial slots of the fused kernel
     uint32_t* err;         // device error flags (bit 0: a bounded wait ran out)
     uint32_t spin_limit;   // polls before a fused wait gives up
 };

@@ -41,13 +41,12 @@ bool sizes_ok(int64_t B, int64_t V) {
 
 // ----------------------------------------------------------------------------
 // workspace: one per (device, stream), grow-only, zeroed when allocated.
-// Layout is fixed by the allocation's capacity, never by the call, so the
-// fused kernel's counters stay at the same addresses (and at zero between
-// calls) whatever B the calls use:
-//   [0, 256)                 flags (uint32 at offset 0)
-//   [256, 256 + 4 Bcap)      cnt[Bcap]
-//   [.., + 4 Bcap)           gen[Bcap]
-//   [aligned 256, + 8 Pcap)  part[Pcap] (float2)
+// Layout is fixed by the allocation's capacity, never by the call, so row r's
+// fused-kernel slots stay at the same address whatever B and V the calls use
+// (their tags must carry over from call to call):
+//   [0, 256)                          flags (uint32 at offset 0)
+//   [256, 256 + 8 kSlotStride Bcap)   slots[Bcap][kSlotStride] (fused)
+//   [aligned 256, + 8 Pcap)           part[Pcap] (float2, split)
 // ----------------------------------------------------------------------------
 struct Workspace {
     void* base = nullptr;
@@ -57,24 +56,22 @@ struct Workspace {
 
 struct WsView {
     uint32_t* err;
-    uint32_t* cnt;
-    uint32_t* gen;
+    unsigned long long* slots;
     float2* part;
 };
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 int64_t ws_bytes(int64_t bcap, int64_t pcap) {
-    return align256(256 + 8 * bcap) + 8 * pcap;
+    return align256(256 + 8 * tsk::kSlotStride * bcap) + 8 * pcap;
 }
 
 WsView ws_view(const Workspace& w) {
     char* b = static_cast<char*>(w.base);
     WsView v;
     v.err = reinterpret_cast<uint32_t*>(b);
-    v.cnt = reinterpret_cast<uint32_t*>(b + 256);
-    v.gen = reinterpret_cast<uint32_t*>(b + 256 + 4 * w.bcap);
-    v.part = reinterpret_cast<float2*>(b + align256(256 + 8 * w.bcap));
+    v.slots = reinterpret_cast<unsigned long long*>(b + 256);
+    v.part = reinterpret_cast<float2*>(b + align256(256 + 8 * tsk::kSlotStride * w.bcap));
     return v;
 }
 
@@ -158,29 +155,34 @@ ts_status fused_caps(bool vec, int64_t caps[5]) {
 }
 
 // Rows that fit one workgroup's registers go one workgroup per row (single
-// read, no partials). Longer rows go to the fused kernel with the smallest
-// chunk whose grid fits the device at once; if no chunk size fits, the one
-// with the fewest items runs persistent (each workgroup loops over items).
+// read, no partials). Longer rows go to the fused kernel (single read) with
+// 8192-column chunks while a row has at most kSlotStride chunks; longer rows
+// than that take the split pair.
 ts_status choose_plan(int64_t B, int64_t V, bool vec, Plan* p) {
+    (void)B;
+    (void)vec;
     if (V <= tsk::kRowwiseResidentMaxV) {
         *p = Plan{TS_VARIANT_ROWWISE, 0};
         return TS_OK;
     }
-    int64_t caps[5];
-    ts_status st = fused_caps(vec, caps);
-    if (st != TS_OK) return st;
-    for (int i = 0; i < 5; ++i) {
-        if (B * cdiv(V, 1024 * kFs[i]) <= caps[i]) {
-            *p = Plan{TS_VARIANT_FUSED, kFs[i]};
+    for (int f : {8, 16}) {
+        if (cdiv(V, 1024 * f) <= tsk::kSlotStride) {
+            *p = Plan{TS_VARIANT_FUSED, f};
             return TS_OK;
         }
     }
-    if (cdiv(V, 1024 * 16) <= caps[4]) {
-        *p = Plan{TS_VARIANT_FUSED, 16};
-        return TS_OK;
-    }
     *p = Plan{TS_VARIANT_SPLIT, 16};
     return TS_OK;
+}
+
+// Fused grid: about two items per workgroup, so that each workgroup's second
+// chunk is loading while its first waits and stores; never fewer workgroups
+// than chunks per row, never more than the device holds at once.
+int64_t fused_grid(int64_t items, int64_t nch, int64_t cap) {
+    int64_t g = cdiv(items, 2);
+    if (g < nch) g = nch;
+    if (g > cap) g = cap;
+    return g;
 }
 
 ts_status run_softmax(const float* logits, const float* temps, int64_t B, int64_t V, float* out,
@@ -237,20 +239,20 @@ ts_status run_softmax(const float* logits, const float* temps, int64_t B, int64_
         int fi = 0;
         while (kFs[fi] != plan.F) ++fi;
         // The lowest unfinished row must fit the device at once (see ts_fused).
-        if (a.nch > caps[fi] || caps[fi] < 1) return TS_ERR_INVALID_ARGUMENT;
-        if (grid > caps[fi]) grid = caps[fi];
+        if (a.nch > tsk::kSlotStride || a.nch > caps[fi]) return TS_ERR_INVALID_ARGUMENT;
+        grid = fused_grid(a.items, a.nch, caps[fi]);
     } else if (a.items > INT32_MAX) {
         return TS_ERR_INVALID_ARGUMENT;
     }
 
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace* w = nullptr;
-    ts_status st = ws_get(stream, plan.variant == TS_VARIANT_FUSED ? B : 0, a.items, &w);
+    const bool fused = plan.variant == TS_VARIANT_FUSED;
+    ts_status st = ws_get(stream, fused ? B : 0, fused ? 0 : a.items, &w);
     if (st != TS_OK) return st;
     const WsView v = ws_view(*w);
     a.part = v.part;
-    a.cnt = v.cnt;
-    a.gen = v.gen;
+    a.slots = v.slots;
     a.err = v.err;
     if (plan.variant == TS_VARIANT_FUSED) return hip_status(tsk::launch_fused(a, plan.F, vec, grid, stream));
     return hip_status(tsk::launch_split(a, plan.F, vec, stream));

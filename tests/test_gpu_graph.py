@@ -57,13 +57,18 @@ def test_capture_and_replay_softmax_then_sample(variant, chunk):
     assert tsv.ts_device_errors(device=DEV, stream=s) == 0
 
 
-def test_capture_without_reserve_is_refused():
+@pytest.mark.parametrize("variant,chunk", [(tsv.TS_VARIANT_FUSED, 8192), (tsv.TS_VARIANT_SPLIT, 2048)])
+def test_capture_without_reserve_is_refused(variant, chunk):
+    # a fresh stream has no workspace: a captured call must not allocate one
     B, V = 8, 300000
     s = torch.cuda.Stream(device=DEV)
     x = torch.zeros((B, V), dtype=torch.float32, device=DEV)
     t = torch.ones((B,), dtype=torch.float32, device=DEV)
     g = torch.cuda.CUDAGraph()
-    with pytest.raises(tsv.TsError) as ei:
-        with torch.cuda.graph(g, stream=s):
-            tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, 1024)
-    assert ei.value.status == tsv.TS_ERR_NOT_RESERVED
+    err = None
+    with torch.cuda.graph(g, stream=s):
+        try:
+            tsv.ts_softmax_variant(x, t, variant, chunk)
+        except tsv.TsError as e:
+            err = e
+    assert err is not None and err.status == tsv.TS_ERR_NOT_RESERVED

@@ -71,9 +71,9 @@ def _edge_rows(V, C, rng):
     x = (rng.standard_normal((8, V)) * 4).astype(np.float32)
     NEG = np.float32(-np.inf)
     n = (V + C - 1) // C
-    x[0, :C] = NEG                                   # first chunk fully masked
+    x[0, :min(C, V - 1)] = NEG                       # first chunk fully masked
     x[1, C: min(2 * C, V)] = NEG                     # a later chunk fully masked
-    x[2, C: C + C // 2] = NEG                        # half a chunk from its start
+    x[2, min(C, V - 1): C + C // 2] = NEG            # half a chunk from its start
     for c in range(n):                               # first float4 of every chunk
         x[3, c * C: c * C + 4] = NEG
     x[4, :] = NEG                                    # one finite id, in the tail chunk
