@@ -137,6 +137,29 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, kernel_nam
     return out
 
 
+def summarize_trace(trace_dir: str, workload: str, kernel_name: str, kernel_tag: str, command: str) -> str:
+    """Per-kernel duration table from a rocprofv3 --kernel-trace --stats run."""
+    rows = []
+    for p in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = os.path.join(PROFILES, f"{kernel_tag}_{workload}_kernel_trace.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 kernel trace summary for {workload}; dominant kernel {kernel_name}\n")
+        f.write(f"# command: {command}\n")
+        f.write(f"# kernel_source_sha256={kernel_source_hash()}\n")
+        f.write(f"{'kernel':<72} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}\n")
+        for r in rows:
+            name = r["Name"].replace("(anonymous namespace)::", "")
+            f.write(f"{name[:72]:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.3f} "
+                    f"{float(r['MinNs']) / 1e3:>9.3f} {float(r['MaxNs']) / 1e3:>9.3f}\n")
+    return out
+
+
 # ----------------------------------------------------------------------------
 # timing
 # ----------------------------------------------------------------------------
@@ -182,7 +205,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extras", action="store_true", help="skip the hot/copy/sample side measurements")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--counters-command", default="python bench.py --steps 200 --warmup 20 --no-cpu-baseline")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--profile-command", default="python3 bench.py --steps 200 --warmup 20 --no-cpu-baseline",
+                    help="the profiled command, recorded in the summaries")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -195,13 +220,16 @@ def main(argv=None) -> int:
     import temperature_softmax_vocabulary_amd as tsv
     from temperature_softmax_vocabulary_amd import workloads
 
-    if args.summarize_counters:
-        v, c = (args.variant, args.chunk) if args.variant else (None, None)
-        cfg = workloads.CONFIGS[args.workload]
-        plan = tsv.ts_plan(cfg["B"], cfg["V"]) if v is None else (v, c)
-        name, tag = _kernel_names(tsv, plan)
-        print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
-                                 name, tag, args.counters_command))
+    if args.summarize_counters or args.summarize_trace:
+        # host-side parsing only; the plan is given or read from the trace
+        if not args.variant:
+            raise SystemExit("--summarize-* needs --variant and --chunk of the profiled plan")
+        name, tag = _kernel_names(tsv, (args.variant, args.chunk))
+        if args.summarize_trace:
+            print(summarize_trace(args.summarize_trace, args.workload, name, tag, args.profile_command))
+        if args.summarize_counters:
+            print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
+                                     name, tag, args.profile_command))
         return 0
 
     if not torch.cuda.is_available():
@@ -240,7 +268,6 @@ def main(argv=None) -> int:
     print(f"[bench] cold {us:.2f} us/call, device errors {errs}, outputs sane {sane}", file=sys.stderr, flush=True)
 
     gbs = bytes_per_call / us / 1e3
-    launches_per_call = 2 if plan[0] == tsv.TS_VARIANT_SPLIT else 1
     traffic = read_traffic(ktag, w.name)
     result = {
         "metric": METRIC,
@@ -261,7 +288,7 @@ def main(argv=None) -> int:
                    "rotating_sets": nsets, "variant": tsv.VARIANT_NAMES[plan[0]], "chunk": plan[1],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kname,
-                     "achieved": round(bytes_per_call / launches_per_call / us / 1e3 * launches_per_call, 1),
+                     "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
@@ -272,7 +299,7 @@ def main(argv=None) -> int:
         extras = {}
         # hot: the same buffers every call (how the page timed, graph replays of one input)
         def hot(i):
-            tsv.ts_softmax(xs[0], ts[0], out=ys[0])
+            step(0)
         for i in range(20):
             hot(i)
         extras["hot_us_per_call"] = round(_elapsed_us(torch, hot, 200), 3)
@@ -314,6 +341,7 @@ def main(argv=None) -> int:
         dp = torch.cuda.get_device_properties(dev)
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
                             "gcn_arch": getattr(dp, "gcnArchName", "")}
+        extras["kernel_source_sha256"] = kernel_source_hash()
         result["extras"] = extras
 
     if not args.no_cpu_baseline:

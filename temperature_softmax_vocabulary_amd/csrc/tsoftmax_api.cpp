@@ -154,34 +154,41 @@ ts_status fused_caps(bool vec, int64_t caps[5]) {
     return TS_OK;
 }
 
-// Rows that fit one workgroup's registers go one workgroup per row (single
-// read, no partials). Longer rows go to the fused kernel (single read) with
-// 8192-column chunks while a row has at most kSlotStride chunks; longer rows
-// than that take the split pair.
+// The work-split table, from graph-replayed timings on MI355X of every
+// variant and chunk size over B in {1, 3, 8, 16, 64}, V in {151936, 201088,
+// 262144}:
+//  - a row that fits one workgroup's registers: one workgroup per row (single
+//    read, no partials);
+//  - B*V <= 2^21 elements: fused, 4096-column chunks (more, smaller workgroups
+//    win while the launch is latency-bound);
+//  - larger: fused, 16384-column chunks (fewest partials; the persistent grid
+//    overlaps waits with the next chunk's loads);
+//  - rows with more than kSlotStride chunks even at 16384 columns: split pair.
 ts_status choose_plan(int64_t B, int64_t V, bool vec, Plan* p) {
-    (void)B;
     (void)vec;
     if (V <= tsk::kRowwiseResidentMaxV) {
         *p = Plan{TS_VARIANT_ROWWISE, 0};
         return TS_OK;
     }
-    for (int f : {8, 16}) {
-        if (cdiv(V, 1024 * f) <= tsk::kSlotStride) {
-            *p = Plan{TS_VARIANT_FUSED, f};
-            return TS_OK;
-        }
+    if (B * V <= (int64_t(1) << 21) && cdiv(V, 4096) <= tsk::kSlotStride) {
+        *p = Plan{TS_VARIANT_FUSED, 4};
+        return TS_OK;
+    }
+    if (cdiv(V, 16384) <= tsk::kSlotStride) {
+        *p = Plan{TS_VARIANT_FUSED, 16};
+        return TS_OK;
     }
     *p = Plan{TS_VARIANT_SPLIT, 16};
     return TS_OK;
 }
 
-// Fused grid: about two items per workgroup, so that each workgroup's second
-// chunk is loading while its first waits and stores; never fewer workgroups
-// than chunks per row, never more than the device holds at once.
+// Fused grid: one workgroup per item while the device holds them all at once;
+// beyond that the grid is the device's capacity and each workgroup loops over
+// items, loading its next chunk while it waits on the current row. Never
+// fewer workgroups than chunks per row.
 int64_t fused_grid(int64_t items, int64_t nch, int64_t cap) {
-    int64_t g = cdiv(items, 2);
+    int64_t g = items < cap ? items : cap;
     if (g < nch) g = nch;
-    if (g > cap) g = cap;
     return g;
 }
 

@@ -1,0 +1,100 @@
+"""The fused kernel's partial exchange across calls, and its bounded wait.
+
+The fused kernel keeps per-row tagged slots in the stream's workspace from one
+call to the next (their parity tag flips every call). These tests change the
+chunk count per row, the row count and the vocabulary between calls on one
+stream and check every result against the oracle, and they force the bounded
+wait to run out from the host (a one-poll limit) to check that the library
+reports it, never hangs, and recovers on the next call. No kernel faults or
+hangs in any of them: a timed-out wait simply carries on.
+"""
+import numpy as np
+import pytest
+import torch
+
+import temperature_softmax_vocabulary_amd as tsv
+from oracle import softmax_ref
+from temperature_softmax_vocabulary_amd import workloads
+from tests.parity import assert_softmax_matches
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _case(B, V, seed):
+    w = workloads.make(B, V, "quarters", seed=seed)
+    return w, torch.from_numpy(w.logits).to(DEV), torch.from_numpy(w.temps).to(DEV)
+
+
+def test_slot_tags_survive_changing_shapes_on_one_stream():
+    s = torch.cuda.Stream(device=DEV)
+    tsv.ts_reserve(32, 262144, device=DEV, stream=s)
+    seq = [(8, 151936, 4096), (8, 151936, 16384), (32, 201088, 1024), (3, 262144, 2048),
+           (32, 201088, 8192), (8, 151936, 4096), (1, 20000, 1024), (32, 262144, 16384)]
+    with torch.cuda.stream(s):
+        for i, (B, V, chunk) in enumerate(seq):
+            w, x, t = _case(B, V, 77 + i)
+            y = tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, chunk)
+            s.synchronize()
+            print(f"[gpu] call {i}: B={B} V={V} chunk={chunk}", flush=True)
+            assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, what=f"call {i}")
+    assert tsv.ts_device_errors(device=DEV, stream=s) == 0
+
+
+def test_forced_wait_timeout_is_reported_and_recovered():
+    w, x, t = _case(64, 262144, 5)
+    ref = softmax_ref(w.logits, w.temps)
+    s = torch.cuda.Stream(device=DEV)
+    tsv.ts_reserve(64, 262144, device=DEV, stream=s)
+    seen = 0
+    try:
+        tsv.ts_debug_set_spin_limit(1)
+        for _ in range(3):
+            with torch.cuda.stream(s):
+                tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, 4096)
+            try:
+                tsv.ts_device_errors(device=DEV, stream=s)
+            except tsv.TsError as e:
+                assert e.status == tsv.TS_ERR_SYNC_TIMEOUT
+                seen += 1
+    finally:
+        tsv.ts_debug_set_spin_limit(0)
+    assert seen >= 1, "a one-poll wait limit never ran out"
+    with torch.cuda.stream(s):
+        y = tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, 4096)
+        y2 = tsv.ts_softmax(x, t)
+    s.synchronize()
+    assert tsv.ts_device_errors(device=DEV, stream=s) == 0
+    assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, ref, what="after recovery")
+    assert_softmax_matches(y2.cpu().numpy(), w.logits, w.temps, ref, what="after recovery, default plan")
+
+
+def test_two_streams_have_independent_workspaces():
+    w1, x1, t1 = _case(16, 201088, 1)
+    w2, x2, t2 = _case(16, 201088, 2)
+    s1, s2 = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            a = tsv.ts_softmax_variant(x1, t1, tsv.TS_VARIANT_FUSED, 8192)
+        with torch.cuda.stream(s2):
+            b = tsv.ts_softmax_variant(x2, t2, tsv.TS_VARIANT_FUSED, 8192)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in outs:
+        assert_softmax_matches(a.cpu().numpy(), w1.logits, w1.temps, what="stream 1")
+        assert_softmax_matches(b.cpu().numpy(), w2.logits, w2.temps, what="stream 2")
+    assert tsv.ts_device_errors(device=DEV, stream=s1) == 0
+    assert tsv.ts_device_errors(device=DEV, stream=s2) == 0
+
+
+def test_fused_rejects_rows_with_too_many_chunks():
+    # 300000 columns at 1024 per chunk is 293 chunks: more than the 256 slots a row has
+    x = torch.zeros((1, 300000), dtype=torch.float32, device=DEV)
+    t = torch.ones((1,), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, 1024)
+    y = tsv.ts_softmax(x, t)          # the default plan picks a legal split
+    torch.cuda.synchronize()
+    assert np.allclose(y.cpu().numpy(), 1.0 / 300000, rtol=1e-6)
