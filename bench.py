@@ -334,10 +334,22 @@ def main(argv=None) -> int:
         e1.record()
         torch.cuda.synchronize()
         extras["graph_us_per_call"] = round(e0.elapsed_time(e1) * 1000.0 / (reps * nsets * 8), 3)
-        # ts_sample on the same rows, 64 draws each (not part of the metric)
+        # token draws on the same rows, 64 uniforms each (not part of the metric):
+        # ts_sample on written probabilities, and the one-pass softmax + draw
+        # with and without writing the probabilities (cold, rotating sets)
         u = torch.from_numpy(w.uniforms).to(dev)
         ids = torch.empty((B, w.uniforms.shape[1]), dtype=torch.int32, device=dev)
-        extras["sample_us_per_call"] = round(_elapsed_us(torch, lambda i: tsv.ts_sample(ys[0], u, out_ids=ids), 50), 3)
+        for i in range(10):
+            tsv.ts_sample(ys[i % nsets], u, out_ids=ids)
+        extras["sample_us_per_call"] = round(
+            _elapsed_us(torch, lambda i: tsv.ts_sample(ys[i % nsets], u, out_ids=ids), 200), 3)
+        for i in range(10):
+            tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids)
+        extras["softmax_sample_ids_only_us_per_call"] = round(
+            _elapsed_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids), 200), 3)
+        extras["softmax_sample_with_probs_us_per_call"] = round(
+            _elapsed_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids,
+                                                               probs_out=ys[i % nsets]), 200), 3)
         dp = torch.cuda.get_device_properties(dev)
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
                             "gcn_arch": getattr(dp, "gcnArchName", "")}

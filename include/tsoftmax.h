@@ -63,10 +63,11 @@ typedef enum ts_status {
  *   TS_VARIANT_ROWWISE - one workgroup per row, no partials. Reads the logits
  *                        once when the row fits in the workgroup's registers,
  *                        else twice.
- *   TS_VARIANT_FUSED   - one kernel: per-chunk partials are exchanged through
- *                        a per-row arrival counter while each workgroup keeps
- *                        its chunk in registers, then the probs are written.
- *                        Reads the logits once. */
+ *   TS_VARIANT_FUSED   - one kernel: each workgroup keeps its chunk in
+ *                        registers while the per-chunk partials are exchanged
+ *                        through tagged per-row slots in the stream's
+ *                        workspace, then writes the probs. Reads the logits
+ *                        once. Rows of at most 256 chunks. */
 typedef enum ts_variant {
     TS_VARIANT_AUTO = 0,
     TS_VARIANT_SPLIT = 1,
@@ -134,6 +135,29 @@ ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
  */
 ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_t V, int64_t K,
                     int32_t* out_ids, hipStream_t stream);
+
+/*
+ * The softmax and the token draw in one pass over the logits: ts_softmax
+ * followed by ts_sample, without writing and re-reading the probabilities
+ * unless asked to. The draw consumes the softmax as in the scope paragraph of
+ * the pull-request page; every id drawn has a finite logit (results table,
+ * sampling row).
+ *
+ * logits, temps : as for ts_softmax.
+ * uniforms      : [B, K] float32, as for ts_sample.
+ * probs_out     : [B, V] float32 or NULL. If not NULL it receives the same
+ *                 probabilities ts_softmax computes (probs_out == logits is
+ *                 allowed); if NULL the probabilities are never written.
+ * out_ids       : [B, K] int32. The inverse-CDF rule of ts_sample, applied to
+ *                 the probabilities in 64-bit fixed point at the fixed scale
+ *                 2^60 (they sum to 1); -1 for a row with no finite logit.
+ * Limits        : V <= 2,097,152 (256 chunks of 8192 columns per row).
+ * Errors        : as ts_softmax and ts_sample; TS_ERR_INVALID_ARGUMENT also for
+ *                 V above the limit. K == 0 reduces to ts_softmax (or a no-op
+ *                 when probs_out is NULL).
+ */
+ts_status ts_softmax_sample(const float* logits, const float* temps, const float* uniforms, int64_t B,
+                            int64_t V, int64_t K, float* probs_out, int32_t* out_ids, hipStream_t stream);
 
 /*
  * Set aside the workspace for any later call with B <= max_B and

@@ -39,6 +39,7 @@ SIGNATURES = {
     "ts_softmax_variant": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I32, _I32, _P]),
     "ts_plan": (ctypes.c_int, [_I64, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "ts_sample": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P]),
+    "ts_softmax_sample": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     "ts_reserve": (ctypes.c_int, [_I64, _I64, _P]),
     "ts_device_errors": (ctypes.c_int, [_P, ctypes.POINTER(_U32)]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -170,6 +171,38 @@ def ts_sample(probs: torch.Tensor, uniforms: torch.Tensor, out_ids: Optional[tor
         _check(lib().ts_sample(probs.data_ptr(), uniforms.data_ptr(), B, V, K, out_ids.data_ptr(),
                                _stream_handle(probs.device, stream)))
     return out_ids
+
+
+def ts_softmax_sample(logits: torch.Tensor, temps: torch.Tensor, uniforms: torch.Tensor,
+                      out_ids: Optional[torch.Tensor] = None, probs_out=False,
+                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Softmax and inverse-CDF draw in one pass over the logits.
+
+    Returns (ids [B, K] int32, probs [B, V] or None). probs_out: False (do not
+    write the probabilities), True (allocate them) or a [B, V] float32 tensor
+    (may be `logits` itself)."""
+    B, V, _ = _softmax_args(logits, temps, logits)
+    _need(uniforms, "uniforms", torch.float32, 2)
+    if uniforms.shape[0] != B or uniforms.device != logits.device:
+        raise ValueError("uniforms must be [B, K] on the logits' device")
+    K = uniforms.shape[1]
+    if out_ids is None:
+        out_ids = torch.empty((B, K), dtype=torch.int32, device=logits.device)
+    else:
+        _need(out_ids, "out_ids", torch.int32, 2)
+        if tuple(out_ids.shape) != (B, K) or out_ids.device != logits.device:
+            raise ValueError("out_ids must be [B, K] int32 on the logits' device")
+    if probs_out is True:
+        probs = torch.empty_like(logits)
+    elif probs_out is False or probs_out is None:
+        probs = None
+    else:
+        _, _, probs = _softmax_args(logits, temps, probs_out)
+    with torch.cuda.device(logits.device):
+        _check(lib().ts_softmax_sample(logits.data_ptr(), temps.data_ptr(), uniforms.data_ptr(), B, V, K,
+                                       probs.data_ptr() if probs is not None else None, out_ids.data_ptr(),
+                                       _stream_handle(logits.device, stream)))
+    return out_ids, probs
 
 
 def ts_reserve(max_B: int, max_V: int, device=None, stream=None) -> None:

@@ -18,11 +18,19 @@
 // the order in which lanes add. Rounding is <= 0.5 * 2^-s per entry, i.e.
 // about 2^-62 of the row total.
 //
-// One workgroup per row, three sweeps over the row: float sum (scale), exact
-// integer total, then a tile walk with an integer carry that resolves every
-// target inside the tile that holds it.
+// Two kernels:
+//  ts_sample_chunks: (row, chunk) items over a persistent grid, one read of the
+//    probabilities. Each chunk's positive-entry float sum and then its exact
+//    integer sum travel between the row's workgroups through the tagged slots
+//    of ts_exchange.h; the chunk that holds a target resolves it. Used while a
+//    row has at most kSlotStride chunks.
+//  ts_sample_rows: one workgroup per row, three sweeps over the row (float
+//    sum for the scale, exact integer total, then a tile walk with an integer
+//    carry). Any V.
 #include "ts_device.h"
+#include "ts_exchange.h"
 #include "ts_launch.h"
+#include "ts_sample_device.h"
 
 namespace tsk {
 
@@ -43,18 +51,6 @@ __device__ __forceinline__ void load4(const float* __restrict__ row, int64_t col
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (col + e < V) ? row[col + e] : 0.0f;
     }
-}
-
-// q = rint(p * 2^s) for p > 0, else 0 (NaN, zero and negative entries).
-__device__ __forceinline__ uint64_t fixed_point(float p, int s) {
-    if (!(p > 0.0f)) return 0;
-    return static_cast<uint64_t>(rintf(ldexpf(p, s)));
-}
-
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
 }
 
 template <bool VEC>
@@ -85,9 +81,7 @@ __global__ __launch_bounds__(ST) void ts_sample_rows(SampleArgs a) {
         for (int64_t k = t; k < a.K; k += ST) idr[k] = -1;
         return;
     }
-    int ex = 0;
-    frexpf(total, &ex);           // total < 2^ex
-    const int s = 61 - ex;        // every p <= row total, so each q < 2^61 (1 + 2^-20)
+    const int s = scale_exponent(total);
 
     // sweep 2: exact integer total
     uint64_t qs = 0;
@@ -117,10 +111,7 @@ __global__ __launch_bounds__(ST) void ts_sample_rows(SampleArgs a) {
         for (int m = 0; m < KPL; ++m) {
             const int64_t k = kbase + t + static_cast<int64_t>(m) * ST;
             mine[m] = k < a.K;
-            float u = mine[m] ? ur[k] : 0.0f;
-            u = (u == u) ? fminf(fmaxf(u, 0.0f), 1.0f) : 0.0f;
-            uint64_t T = static_cast<uint64_t>(floor(static_cast<double>(u) * static_cast<double>(qtotal)));
-            tgt[m] = T < qtotal ? T : qtotal - 1;
+            tgt[m] = target_of(mine[m] ? ur[k] : 0.0f, qtotal);
         }
         uint64_t carry = 0;
         for (int64_t c0 = 0; c0 < a.V; c0 += STILE) {
@@ -172,9 +163,164 @@ __global__ __launch_bounds__(ST) void ts_sample_rows(SampleArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// chunked: one read of the probabilities
+// ---------------------------------------------------------------------------
+constexpr int CT = 256;
+constexpr int CW = CT / kWave;
+
+template <int F>
+constexpr size_t sample_chunk_lds() {
+    return resolve_lds_bytes<CT, F>();
+}
+
+template <int F, bool VEC>
+__global__ __launch_bounds__(CT) void ts_sample_chunks(SampleArgs a) {
+    extern __shared__ __align__(16) float dyn[];
+    __shared__ float redf[CW];
+    __shared__ uint64_t red64[CW];
+    __shared__ float row_sum;
+    __shared__ uint64_t row_base, row_total;
+    constexpr int C = CT * 4 * F;
+    const int lane = threadIdx.x;
+    int64_t item = blockIdx.x;
+    if (item >= a.items) return;
+    // the next item's chunk is loaded while this one waits on its row
+    float p[4 * F], np[4 * F];
+    unsigned long long own_f = 0, own_q = 0, next_f = 0, next_q = 0;
+    {
+        const int64_t row = item / a.nch, c = item - row * a.nch;
+        load_chunk<CT, F, VEC, true>(a.probs + row * a.V, c * C, a.V, p, 0.0f);
+        if (lane == 0) {
+            own_f = slot_load(a.fslots + row * kSlotStride + c);
+            own_q = slot_load(a.qslots + row * kSlotStride + c);
+        }
+    }
+    for (; item < a.items; item += gridDim.x) {
+        const int64_t row = item / a.nch;
+        const int64_t c = item - row * a.nch;
+        unsigned long long* fs = a.fslots + row * kSlotStride;
+        unsigned long long* qs = a.qslots + row * kSlotStride;
+        const int64_t nitem = item + gridDim.x;
+        if (nitem < a.items) {
+            const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
+            load_chunk<CT, F, VEC, true>(a.probs + nr * a.V, nc * C, a.V, np, 0.0f);
+            if (lane == 0) {
+                next_f = slot_load(a.fslots + nr * kSlotStride + nc);
+                next_q = slot_load(a.qslots + nr * kSlotStride + nc);
+            }
+        }
+        // exchange 1: float sum of the positive entries -> the row's scale
+        float fsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4 * F; ++i) fsum += (p[i] > 0.0f) ? p[i] : 0.0f;
+        fsum = block_reduce<SumOp, CW>(fsum, redf);
+        if (lane < kWave) {
+            const unsigned long long tf = next_tag(own_f);
+            publish(fs, c, a.nch, tf, __float_as_uint(fsum));
+            unsigned long long v[kSlotsPerLane];
+            wait_row(fs, a.nch, tf, 0ull, v, a.spin_limit, a.err);
+            float tot = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kSlotsPerLane; ++j) tot += __uint_as_float(static_cast<uint32_t>(v[j]));
+            tot = wave_reduce<SumOp>(tot);   // same slots, same order in every workgroup of the row
+            if (lane == 0) row_sum = tot;
+        }
+        __syncthreads();
+        const float total = row_sum;
+        const bool valid = total > 0.0f && total < __builtin_huge_valf();
+        const int s = valid ? scale_exponent(total) : 0;
+        // exchange 2: exact integer sums (published even for an invalid row, to keep the tags)
+        uint64_t qc = 0;
+        if (valid) {
+#pragma unroll
+            for (int i = 0; i < 4 * F; ++i) qc += fixed_point(p[i], s);
+        }
+        qc = block_sum_u64<CW>(qc, red64);
+        if (lane < kWave) {
+            const unsigned long long tq = next_tag(own_q);
+            publish(qs, c, a.nch, tq, qc);
+            unsigned long long v[kSlotsPerLane];
+            wait_row(qs, a.nch, tq, 0ull, v, a.spin_limit, a.err);
+            uint64_t before = 0, tot = 0;
+#pragma unroll
+            for (int j = 0; j < kSlotsPerLane; ++j) {
+                const int64_t i = lane + static_cast<int64_t>(j) * kWave;
+                tot += v[j];
+                before += (i < c) ? v[j] : 0;
+            }
+            before = wave_sum_u64(before);
+            tot = wave_sum_u64(tot);
+            if (lane == 0) {
+                row_base = before;
+                row_total = tot;
+            }
+        }
+        __syncthreads();
+        const uint64_t base = row_base, Q = row_total;
+        const float* urow = a.uniforms + row * a.K;
+        int32_t* idrow = a.out_ids + row * a.K;
+        if (!valid || Q == 0) {
+            if (c == 0)
+                for (int64_t kk = lane; kk < a.K; kk += CT) idrow[kk] = -1;
+        } else {
+            const float* pr = a.probs + row * a.V;
+            const int64_t c0 = c * C;
+            const int64_t V = a.V;
+            auto fetch = [=](int j, int o, float (&v)[4]) { load_group4<CT>(pr, c0, V, j, o, 0.0f, v); };
+            resolve_chunk<CT, F>(p, reinterpret_cast<unsigned char*>(dyn), s, base, qc, Q, c0, urow, a.K, idrow,
+                                 fetch);
+        }
+#pragma unroll
+        for (int i = 0; i < 4 * F; ++i) p[i] = np[i];
+        own_f = next_f;
+        own_q = next_q;
+        __syncthreads();   // row broadcasts are rewritten by the next item
+    }
+}
+
+template <int F, bool VEC>
+hipError_t sample_chunks_impl(const SampleArgs& a, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((ts_sample_chunks<F, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(CT),
+                       sample_chunk_lds<F>(), s, a);
+    return hipGetLastError();
+}
+
+template <int F, bool VEC>
+hipError_t sample_cap_impl(int64_t* cap) {
+    int dev = 0, per_cu = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ts_sample_chunks<F, VEC>),
+                                                     CT, sample_chunk_lds<F>());
+    if (e != hipSuccess) return e;
+    *cap = static_cast<int64_t>(per_cu) * cus;
+    return hipSuccess;
+}
+
+#define TS_SAMPLE_DISPATCH(IMPL, F, VEC, ...)                                                   \
+    do {                                                                                        \
+        switch (F) {                                                                            \
+            case 4: return VEC ? IMPL<4, true>(__VA_ARGS__) : IMPL<4, false>(__VA_ARGS__);     \
+            case 8: return VEC ? IMPL<8, true>(__VA_ARGS__) : IMPL<8, false>(__VA_ARGS__);     \
+            default: return hipErrorInvalidValue;                                               \
+        }                                                                                       \
+    } while (0)
+
 }  // namespace
 
-hipError_t launch_sample(const SampleArgs& a, bool vec, hipStream_t s) {
+hipError_t launch_sample_chunks(const SampleArgs& a, int F, bool vec, int64_t grid, hipStream_t s) {
+    TS_SAMPLE_DISPATCH(sample_chunks_impl, F, vec, a, grid, s);
+}
+
+hipError_t sample_resident_capacity(int F, bool vec, int64_t* cap) {
+    TS_SAMPLE_DISPATCH(sample_cap_impl, F, vec, cap);
+}
+
+hipError_t launch_sample_rows(const SampleArgs& a, bool vec, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(a.B));
     if (vec) hipLaunchKernelGGL((ts_sample_rows<true>), grid, dim3(ST), 0, s, a);
     else hipLaunchKernelGGL((ts_sample_rows<false>), grid, dim3(ST), 0, s, a);

@@ -20,7 +20,9 @@
 //  rowwise : one workgroup per row; the row sits in registers when it fits
 //            (read once), else an online (m, l) sweep and a write sweep.
 #include "ts_device.h"
+#include "ts_exchange.h"
 #include "ts_launch.h"
+#include "ts_sample_device.h"
 
 namespace tsk {
 
@@ -102,56 +104,54 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 //
 // Work items are (row, chunk) pairs, item = row * nch + chunk. Workgroup w
 // handles items w, w + gridDim.x, ... in order, and issues the loads of its
-// next item before it waits on the current row, so a workgroup's wait and
-// stores overlap its next reads. The host launches no more workgroups than the
-// device holds at once and at least nch of them: every chunk of the lowest
-// unfinished row is then done or resident, so the row always completes. Each
-// wait is still bounded (spin_limit polls; running out raises bit 0 of *err).
+// next item before it waits on the current row, so a workgroup's waits and
+// stores overlap its next reads. The chunk partials (pm, pl) travel through
+// the tagged slots of ts_exchange.h (no fence, no contended read-modify-write:
+// either costs microseconds per workgroup on a multi-XCD part). The host
+// launches no more workgroups than the device holds at once and at least nch.
 //
-// Exchange of chunk partials, with no fence and no contended read-modify-write
-// (both cost microseconds per workgroup on a multi-XCD part): each row owns
-// kSlotStride 64-bit slots. A slot holds (pm, pl) of one chunk and, in pl's
-// sign bit (pl >= 0, so the bit is free), a parity tag. Between calls every
-// slot of a row carries the same tag t. In a call, the workgroup of chunk c
-// reads its own slot (it is the slot's only writer in the call, so it reads
-// t), stores (pm, pl, t ^ 1) with one 64-bit atomic store, and also stores tag
-// t ^ 1 into the row's unused slots c + nch, c + 2 nch, ... Readers poll the
-// row's nch slots with 64-bit atomic loads until each shows t ^ 1; the value
-// that shows the new tag is the data itself. Only per-location coherence of
-// relaxed agent-scope atomics is used, plus the ordering between launches on
-// a stream. After the call every slot of the row carries t ^ 1 again, whatever
-// nch the next call uses.
+// MODE kFusedProbs writes the probabilities. kFusedProbsIds and kFusedIds also
+// draw token ids by inverse CDF (ts_sample_device.h) from the probabilities
+// the chunk holds in registers, through a second exchange of the chunks'
+// exact integer sums; kFusedIds skips writing the probabilities.
 // ---------------------------------------------------------------------------
-template <int F>
+template <int F, int MODE>
 struct FusedOcc {
-    // registers hold the current and the next chunk: 8 F floats per lane
-    static constexpr int waves_per_eu = F <= 4 ? 8 : (F == 8 ? 4 : 2);
+    // registers hold the current and the next chunk (8 F floats per lane);
+    // the sampling modes need about 60 more for the second exchange
+    static constexpr int probs_only = F <= 4 ? 8 : (F == 8 ? 4 : 2);
+    static constexpr int waves_per_eu = MODE == kFusedProbs ? probs_only : (F <= 2 ? 4 : (F == 4 ? 3 : 2));
 };
 
-constexpr unsigned long long kTagBit = 1ull << 63;
-
-__device__ __forceinline__ unsigned long long slot_load(const unsigned long long* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void slot_store(unsigned long long* p, unsigned long long v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// LDS of a sampling mode: see resolve_chunk.
+template <int F>
+constexpr size_t fused_sample_lds() {
+    return resolve_lds_bytes<NT, F>();
 }
 
-template <int F, bool VEC>
-__global__ __launch_bounds__(NT, FusedOcc<F>::waves_per_eu) void ts_fused(SoftmaxArgs a) {
+template <int F, bool VEC, int MODE>
+__global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fused(SoftmaxArgs a) {
+    extern __shared__ __align__(16) float dyn[];
     __shared__ float red[NW];
+    __shared__ uint64_t red64[NW];
     __shared__ float chunk_scale;
+    __shared__ uint64_t row_base, row_total;
+    constexpr bool SAMPLE = MODE != kFusedProbs;
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
     int64_t item = blockIdx.x;
     if (item >= a.items) return;
 
     float x[4 * F], nx[4 * F];
-    unsigned long long own = 0, next_own = 0;   // lane 0: old value of the item's own slot
+    // lane 0: old values of the item's own slots (and of the next item's)
+    unsigned long long own = 0, next_own = 0, own_q = 0, next_own_q = 0;
     {
         const int64_t row = item / a.nch, c = item - row * a.nch;
         load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x);
-        if (lane == 0) own = slot_load(a.slots + row * kSlotStride + c);
+        if (lane == 0) {
+            own = slot_load(a.slots + row * kSlotStride + c);
+            if (SAMPLE) own_q = slot_load(a.qslots + row * kSlotStride + c);
+        }
     }
     for (; item < a.items; item += gridDim.x) {
         const int64_t row = item / a.nch;
@@ -173,65 +173,102 @@ __global__ __launch_bounds__(NT, FusedOcc<F>::waves_per_eu) void ts_fused(Softma
         }
         const float pl = block_reduce<SumOp, NW>(l, red);
 
-        // publish with the flipped tag
-        const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(own >> 32));
-        const unsigned long long tag = static_cast<unsigned long long>((hi >> 31) ^ 1u) << 63;
-        if (lane == 0)
-            slot_store(rs + c, tag | (static_cast<unsigned long long>(__float_as_uint(pl)) << 32) | __float_as_uint(pm));
+        const unsigned long long tag = next_tag(own);   // wave-uniform, all lanes
         if (lane < kWave)
-            for (int64_t j = c + a.nch * (1 + lane); j < kSlotStride; j += a.nch * kWave) slot_store(rs + j, tag);
+            publish(rs, c, a.nch,
+                    tag, (static_cast<unsigned long long>(__float_as_uint(pl)) << 32) | __float_as_uint(pm));
 
         // prefetch the next item (a later row: gridDim.x >= nch)
         const int64_t nitem = item + gridDim.x;
         if (nitem < a.items) {
             const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
             load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx);
-            if (lane == 0) next_own = slot_load(a.slots + nr * kSlotStride + nc);
+            if (lane == 0) {
+                next_own = slot_load(a.slots + nr * kSlotStride + nc);
+                if (SAMPLE) next_own_q = slot_load(a.qslots + nr * kSlotStride + nc);
+            }
         }
 
-        // wave 0 waits for the row's slots and combines them (nch <= kSlotStride,
-        // so each lane holds at most kSlotStride / 64 slot values)
+        // wave 0 waits for the row's partials and combines them: gm = max pm,
+        // gl = sum pl exp2((pm - gm) k), a fully masked chunk adding exactly 0
         if (lane < kWave) {
-            constexpr int SPL = kSlotStride / kWave;
-            float vm[SPL], vl[SPL];
+            unsigned long long v[kSlotsPerLane];
+            const unsigned long long absent = __float_as_uint(kNegInf);   // pm = -inf, pl = 0
+            wait_row(rs, a.nch, tag, absent, v, a.spin_limit, a.err);
             float mm = kNegInf;
-            uint32_t polls = 0;
 #pragma unroll
-            for (int j = 0; j < SPL; ++j) {
-                const int64_t i = lane + static_cast<int64_t>(j) * kWave;
-                vm[j] = kNegInf;
-                vl[j] = 0.0f;
-                if (i < a.nch) {
-                    unsigned long long v = slot_load(rs + i);
-                    while ((v & kTagBit) != tag) {
-                        if (++polls > a.spin_limit) {
-                            __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                        v = slot_load(rs + i);
-                    }
-                    vm[j] = __uint_as_float(static_cast<uint32_t>(v));
-                    vl[j] = __uint_as_float(static_cast<uint32_t>(v >> 32) & 0x7fffffffu);
-                    mm = fmaxf(mm, vm[j]);
-                }
-            }
+            for (int j = 0; j < kSlotsPerLane; ++j) mm = fmaxf(mm, __uint_as_float(static_cast<uint32_t>(v[j])));
             const float gsh = guarded_shift(wave_reduce<MaxOp>(mm));
             float ll = 0.0f;
 #pragma unroll
-            for (int j = 0; j < SPL; ++j) ll += (vm[j] == kNegInf) ? 0.0f : vl[j] * exp2_hw((vm[j] - gsh) * k);
+            for (int j = 0; j < kSlotsPerLane; ++j) {
+                const float vm = __uint_as_float(static_cast<uint32_t>(v[j]));
+                const float vl = __uint_as_float(static_cast<uint32_t>(v[j] >> 32));
+                ll += (vm == kNegInf) ? 0.0f : vl * exp2_hw((vm - gsh) * k);
+            }
             const float gl = wave_reduce<SumOp>(ll);
             if (lane == 0) chunk_scale = (pm == kNegInf) ? 0.0f : exp2_hw((pm - gsh) * k) * (1.0f / gl);
         }
         __syncthreads();
         const float scale = chunk_scale;
 #pragma unroll
-        for (int i = 0; i < 4 * F; ++i) x[i] *= scale;
-        store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+        for (int i = 0; i < 4 * F; ++i) x[i] *= scale;    // the probabilities
+        if (MODE == kFusedProbs) store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+
+        if constexpr (SAMPLE) {
+            // second exchange: exact integer sums of the chunks' fixed-point weights
+            uint64_t qc = 0;
+#pragma unroll
+            for (int i = 0; i < 4 * F; ++i) qc += fixed_point(x[i], kProbScaleExp);
+            qc = block_sum_u64<NW>(qc, red64);
+            const unsigned long long tq = next_tag(own_q);
+            unsigned long long* qs = a.qslots + row * kSlotStride;
+            if (lane < kWave) {
+                publish(qs, c, a.nch, tq, qc);
+                unsigned long long v[kSlotsPerLane];
+                wait_row(qs, a.nch, tq, 0ull, v, a.spin_limit, a.err);
+                uint64_t before = 0, total = 0;
+#pragma unroll
+                for (int j = 0; j < kSlotsPerLane; ++j) {
+                    const int64_t i = lane + static_cast<int64_t>(j) * kWave;
+                    total += v[j];
+                    before += (i < c) ? v[j] : 0;
+                }
+                before = wave_sum_u64(before);
+                total = wave_sum_u64(total);
+                if (lane == 0) {
+                    row_base = before;
+                    row_total = total;
+                }
+            }
+            __syncthreads();
+            const uint64_t base = row_base, Q = row_total;
+            const float* urow = a.uniforms + row * a.K;
+            int32_t* idrow = a.out_ids + row * a.K;
+            if (Q == 0) {   // no positive probability (a row with no finite logit)
+                if (c == 0)
+                    for (int64_t kk = lane; kk < a.K; kk += NT) idrow[kk] = -1;
+            } else {
+                const float* xr = a.logits + row * a.V;
+                const int64_t c0 = c * C;
+                const int64_t V = a.V;
+                // p = exp2((x - sh) k) * scale, as computed above for x[]
+                auto fetch = [=](int j, int o, float (&v)[4]) {
+                    load_group4<NT>(xr, c0, V, j, o, kNegInf, v);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = exp2_hw((v[e] - sh) * k) * scale;
+                };
+                resolve_chunk<NT, F>(x, reinterpret_cast<unsigned char*>(dyn), kProbScaleExp, base, qc, Q, c0,
+                                     urow, a.K, idrow, fetch);
+            }
+            own_q = next_own_q;
+            // written only now: with probs_out == logits the draw above re-reads logits
+            if (MODE == kFusedProbsIds) store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+        }
 #pragma unroll
         for (int i = 0; i < 4 * F; ++i) x[i] = nx[i];
         own = next_own;
-        __syncthreads();   // chunk_scale is rewritten by the next item
+        __syncthreads();   // chunk_scale and the row broadcasts are rewritten by the next item
     }
 }
 
@@ -315,27 +352,36 @@ hipError_t split_impl(const SoftmaxArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int F, bool VEC, int MODE>
+const void* fused_fn() { return reinterpret_cast<const void*>(&ts_fused<F, VEC, MODE>); }
+
 template <int F, bool VEC>
-hipError_t fused_impl(const SoftmaxArgs& a, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((ts_fused<F, VEC>), dim3(static_cast<uint32_t>(grid)), dim3(NT), 0, s, a);
+size_t fused_lds(int mode) { return mode == kFusedProbs ? 0 : fused_sample_lds<F>(); }
+
+template <int F, bool VEC>
+hipError_t fused_impl(const SoftmaxArgs& a, int mode, int64_t grid, hipStream_t s) {
+    const dim3 g(static_cast<uint32_t>(grid));
+    const size_t lds = fused_lds<F, VEC>(mode);
+    if (mode == kFusedProbs) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbs>), g, dim3(NT), lds, s, a);
+    else if (mode == kFusedProbsIds) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbsIds>), g, dim3(NT), lds, s, a);
+    else hipLaunchKernelGGL((ts_fused<F, VEC, kFusedIds>), g, dim3(NT), lds, s, a);
     return hipGetLastError();
 }
 
 template <int F, bool VEC>
-hipError_t fused_cap_impl(int64_t* cap) {
-    int dev = 0, per_cu = 0;
+hipError_t fused_cap_impl(int mode, int64_t* cap) {
+    int dev = 0, per_cu = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    hipDeviceProp_t prop;
-    e = hipGetDeviceProperties(&prop, dev);
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ts_fused<F, VEC>),
-                                                     NT, 0);
+    const void* fn = mode == kFusedProbs ? fused_fn<F, VEC, kFusedProbs>()
+                     : mode == kFusedProbsIds ? fused_fn<F, VEC, kFusedProbsIds>() : fused_fn<F, VEC, kFusedIds>();
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, fused_lds<F, VEC>(mode));
     if (e != hipSuccess) return e;
-    *cap = static_cast<int64_t>(per_cu) * prop.multiProcessorCount;
+    *cap = static_cast<int64_t>(per_cu) * cus;
     return hipSuccess;
 }
-
 
 #define TS_DISPATCH_F(IMPL, F, VEC, ...)                                       \
     do {                                                                       \
@@ -355,12 +401,12 @@ hipError_t launch_split(const SoftmaxArgs& a, int F, bool vec, hipStream_t s) {
     TS_DISPATCH_F(split_impl, F, vec, a, s);
 }
 
-hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int64_t grid, hipStream_t s) {
-    TS_DISPATCH_F(fused_impl, F, vec, a, grid, s);
+hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int mode, int64_t grid, hipStream_t s) {
+    TS_DISPATCH_F(fused_impl, F, vec, a, mode, grid, s);
 }
 
-hipError_t fused_resident_capacity(int F, bool vec, int64_t* cap) {
-    TS_DISPATCH_F(fused_cap_impl, F, vec, cap);
+hipError_t fused_resident_capacity(int F, bool vec, int mode, int64_t* cap) {
+    TS_DISPATCH_F(fused_cap_impl, F, vec, mode, cap);
 }
 
 hipError_t launch_rowwise(const SoftmaxArgs& a, bool vec, hipStream_t s) {

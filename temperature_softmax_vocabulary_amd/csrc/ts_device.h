@@ -85,21 +85,24 @@ __device__ __forceinline__ float block_reduce(float v, float* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunk access. A chunk is C = NT * 4 * F consecutive columns of one row.
-// Vector path (16-byte aligned row, V % 4 == 0): lane t of the workgroup owns
-// the float4 at column c0 + (j * NT + t) * 4 for j in [0, F), so each wave64
-// load instruction covers 1 KiB of contiguous memory. Scalar path: lane t owns
-// columns c0 + j * NT + t for j in [0, 4F). Columns at or past V read as -inf.
+// Chunk access. A chunk is C = NT * 4 * F consecutive columns of one row, in F
+// groups of NT * 4 columns. Lane t of the workgroup owns the 4 consecutive
+// columns c0 + (j * NT + t) * 4 + e, e in [0, 4), of every group j, held in
+// x[4 j + e]; within a group, lane order is column order. Vector path (16-byte
+// aligned row, V % 4 == 0): one float4 load per group, so each wave64 load
+// instruction covers 1 KiB of contiguous memory. Scalar path: four bounds-
+// checked 4-byte loads per group. Columns at or past V read as `fill` (-inf
+// for logits: they add nothing to a max or to a sum of exponentials).
 // ---------------------------------------------------------------------------
 template <int NT, int F, bool VEC, bool NT_LOAD>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t c0, int64_t V,
-                                           float (&x)[4 * F]) {
+                                           float (&x)[4 * F], float fill = kNegInf) {
     const int t = threadIdx.x;
     if constexpr (VEC) {
 #pragma unroll
         for (int j = 0; j < F; ++j) {
             const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
-            f4 v = {kNegInf, kNegInf, kNegInf, kNegInf};
+            f4 v = {fill, fill, fill, fill};
             if (col < V) {
                 const f4* p = reinterpret_cast<const f4*>(row + col);
                 if constexpr (NT_LOAD) v = __builtin_nontemporal_load(p);
@@ -109,14 +112,17 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4 * F; ++j) {
-            const int64_t col = c0 + static_cast<int64_t>(j) * NT + t;
-            float v = kNegInf;
-            if (col < V) {
-                if constexpr (NT_LOAD) v = __builtin_nontemporal_load(row + col);
-                else v = row[col];
+        for (int j = 0; j < F; ++j) {
+            const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = fill;
+                if (col + e < V) {
+                    if constexpr (NT_LOAD) v = __builtin_nontemporal_load(row + col + e);
+                    else v = row[col + e];
+                }
+                x[4 * j + e] = v;
             }
-            x[j] = v;
         }
     }
 }
@@ -138,11 +144,14 @@ __device__ __forceinline__ void store_chunk(float* __restrict__ row, int64_t c0,
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4 * F; ++j) {
-            const int64_t col = c0 + static_cast<int64_t>(j) * NT + t;
-            if (col < V) {
-                if constexpr (NT_STORE) __builtin_nontemporal_store(y[j], row + col);
-                else row[col] = y[j];
+        for (int j = 0; j < F; ++j) {
+            const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (col + e < V) {
+                    if constexpr (NT_STORE) __builtin_nontemporal_store(y[4 * j + e], row + col + e);
+                    else row[col + e] = y[4 * j + e];
+                }
             }
         }
     }

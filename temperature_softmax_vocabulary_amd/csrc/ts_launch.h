@@ -13,9 +13,16 @@ constexpr int kChunkThreads = 256;
 constexpr int kMinChunk = 1024;
 constexpr int kMaxChunk = 16384;
 
-// Slots per row for the fused kernel's partial exchange: it runs only when a
-// row has at most this many chunks.
+// Slots per row for the in-kernel exchanges (ts_exchange.h): the chunked
+// kernels run only when a row has at most this many chunks. Each stream's
+// workspace holds three slot sets: softmax partials (pm, pl), sampler float
+// sums, sampler integer sums.
 constexpr int64_t kSlotStride = 256;
+constexpr int kSlotSets = 3;
+constexpr int kSetPartials = 0, kSetFloatSums = 1, kSetIntSums = 2;
+
+// Fixed-point scale 2^60 for normalised probabilities (each <= 1, sum ~ 1).
+constexpr int kProbScaleExp = 60;
 
 // Largest row the resident one-workgroup-per-row kernel holds in registers.
 constexpr int kRowwiseThreads = 1024;
@@ -30,15 +37,23 @@ struct SoftmaxArgs {
     int64_t nch;           // chunks per row (split, fused)
     int64_t items;         // B * nch
     float2* part;          // [B * nch] chunk partials (pm, pl) of the split kernels
-    unsigned long long* slots;  // [B * kSlotStride] tagged partial slots of the fused kernel
+    unsigned long long* slots;   // [B * kSlotStride] tagged (pm, pl) slots of the fused kernel
+    unsigned long long* qslots;  // [B * kSlotStride] tagged integer-sum slots (fused sampling)
     uint32_t* err;         // device error flags (bit 0: a bounded wait ran out)
     uint32_t spin_limit;   // polls before a fused wait gives up
+    // fused softmax-and-sample only
+    const float* uniforms; // [B, K]
+    int32_t* out_ids;      // [B, K]
+    int64_t K;
 };
 
+// Fused kernel modes: probabilities only; probabilities and ids; ids only.
+constexpr int kFusedProbs = 0, kFusedProbsIds = 1, kFusedIds = 2;
+
 hipError_t launch_split(const SoftmaxArgs& a, int F, bool vec, hipStream_t s);
-hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int64_t grid, hipStream_t s);
+hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int mode, int64_t grid, hipStream_t s);
 // Workgroups of the fused kernel that one device holds at once (occupancy x CUs).
-hipError_t fused_resident_capacity(int F, bool vec, int64_t* cap);
+hipError_t fused_resident_capacity(int F, bool vec, int mode, int64_t* cap);
 hipError_t launch_rowwise(const SoftmaxArgs& a, bool vec, hipStream_t s);
 
 struct SampleArgs {
@@ -48,8 +63,19 @@ struct SampleArgs {
     int64_t B;
     int64_t V;
     int64_t K;
+    // chunked kernel only
+    int64_t nch;
+    int64_t items;
+    unsigned long long* fslots;  // [B * kSlotStride] tagged float-sum slots
+    unsigned long long* qslots;  // [B * kSlotStride] tagged integer-sum slots
+    uint32_t* err;
+    uint32_t spin_limit;
 };
-hipError_t launch_sample(const SampleArgs& a, bool vec, hipStream_t s);
+// One workgroup per row, three sweeps (any V).
+hipError_t launch_sample_rows(const SampleArgs& a, bool vec, hipStream_t s);
+// Chunked, one read: (row, chunk) items over a persistent grid (nch <= kSlotStride).
+hipError_t launch_sample_chunks(const SampleArgs& a, int F, bool vec, int64_t grid, hipStream_t s);
+hipError_t sample_resident_capacity(int F, bool vec, int64_t* cap);
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, bool vec, hipStream_t s);
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <utility>
 
@@ -42,11 +43,11 @@ bool sizes_ok(int64_t B, int64_t V) {
 // ----------------------------------------------------------------------------
 // workspace: one per (device, stream), grow-only, zeroed when allocated.
 // Layout is fixed by the allocation's capacity, never by the call, so row r's
-// fused-kernel slots stay at the same address whatever B and V the calls use
-// (their tags must carry over from call to call):
-//   [0, 256)                          flags (uint32 at offset 0)
-//   [256, 256 + 8 kSlotStride Bcap)   slots[Bcap][kSlotStride] (fused)
-//   [aligned 256, + 8 Pcap)           part[Pcap] (float2, split)
+// slots stay at the same address whatever B and V the calls use (their tags
+// carry over from call to call, ts_exchange.h):
+//   [0, 256)                                   flags (uint32 at offset 0)
+//   [256, 256 + 8 kSlotStride Bcap kSlotSets)  slots[kSlotSets][Bcap][kSlotStride]
+//   [aligned 256, + 8 Pcap)                    part[Pcap] (float2, split)
 // ----------------------------------------------------------------------------
 struct Workspace {
     void* base = nullptr;
@@ -56,22 +57,25 @@ struct Workspace {
 
 struct WsView {
     uint32_t* err;
-    unsigned long long* slots;
+    unsigned long long* sets[tsk::kSlotSets];
     float2* part;
 };
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+int64_t slot_bytes(int64_t bcap) { return 8 * tsk::kSlotStride * bcap * tsk::kSlotSets; }
+
 int64_t ws_bytes(int64_t bcap, int64_t pcap) {
-    return align256(256 + 8 * tsk::kSlotStride * bcap) + 8 * pcap;
+    return align256(256 + slot_bytes(bcap)) + 8 * pcap;
 }
 
 WsView ws_view(const Workspace& w) {
     char* b = static_cast<char*>(w.base);
     WsView v;
     v.err = reinterpret_cast<uint32_t*>(b);
-    v.slots = reinterpret_cast<unsigned long long*>(b + 256);
-    v.part = reinterpret_cast<float2*>(b + align256(256 + 8 * tsk::kSlotStride * w.bcap));
+    for (int k = 0; k < tsk::kSlotSets; ++k)
+        v.sets[k] = reinterpret_cast<unsigned long long*>(b + 256) + static_cast<int64_t>(k) * tsk::kSlotStride * w.bcap;
+    v.part = reinterpret_cast<float2*>(b + align256(256 + slot_bytes(w.bcap)));
     return v;
 }
 
@@ -136,21 +140,24 @@ struct Plan {
     int F;   // chunk = 1024 * F (split, fused)
 };
 
-// Fused-kernel residency per F on the current device (cached per device).
-ts_status fused_caps(bool vec, int64_t caps[5]) {
+// Workgroups one device holds at once, per kernel (cached per device):
+// kind 0..2 = fused kernel in that mode, kind 3 = chunked sampler.
+ts_status resident_cap(int kind, int F, bool vec, int64_t* cap) {
     static std::mutex mu;
-    static std::map<std::pair<int, bool>, std::array<int64_t, 5>> cache;
+    static std::map<std::tuple<int, int, int, bool>, int64_t> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return TS_ERR_HIP;
     std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find({dev, vec});
+    const auto key = std::make_tuple(dev, kind, F, vec);
+    auto it = cache.find(key);
     if (it == cache.end()) {
-        std::array<int64_t, 5> c{};
-        for (int i = 0; i < 5; ++i)
-            if (tsk::fused_resident_capacity(kFs[i], vec, &c[i]) != hipSuccess) return TS_ERR_HIP;
-        it = cache.emplace(std::make_pair(dev, vec), c).first;
+        int64_t c = 0;
+        const hipError_t e = kind == 3 ? tsk::sample_resident_capacity(F, vec, &c)
+                                       : tsk::fused_resident_capacity(F, vec, kind, &c);
+        if (e != hipSuccess) return TS_ERR_HIP;
+        it = cache.emplace(key, c).first;
     }
-    for (int i = 0; i < 5; ++i) caps[i] = it->second[i];
+    *cap = it->second;
     return TS_OK;
 }
 
@@ -240,14 +247,12 @@ ts_status run_softmax(const float* logits, const float* temps, int64_t B, int64_
     a.items = B * a.nch;
     int64_t grid = a.items;
     if (plan.variant == TS_VARIANT_FUSED) {
-        int64_t caps[5];
-        ts_status st = fused_caps(vec, caps);
+        int64_t cap = 0;
+        ts_status st = resident_cap(tsk::kFusedProbs, plan.F, vec, &cap);
         if (st != TS_OK) return st;
-        int fi = 0;
-        while (kFs[fi] != plan.F) ++fi;
-        // The lowest unfinished row must fit the device at once (see ts_fused).
-        if (a.nch > tsk::kSlotStride || a.nch > caps[fi]) return TS_ERR_INVALID_ARGUMENT;
-        grid = fused_grid(a.items, a.nch, caps[fi]);
+        // The lowest unfinished row must fit the device at once (ts_exchange.h).
+        if (a.nch > tsk::kSlotStride || a.nch > cap) return TS_ERR_INVALID_ARGUMENT;
+        grid = fused_grid(a.items, a.nch, cap);
     } else if (a.items > INT32_MAX) {
         return TS_ERR_INVALID_ARGUMENT;
     }
@@ -259,10 +264,22 @@ ts_status run_softmax(const float* logits, const float* temps, int64_t B, int64_
     if (st != TS_OK) return st;
     const WsView v = ws_view(*w);
     a.part = v.part;
-    a.slots = v.slots;
+    a.slots = v.sets[tsk::kSetPartials];
+    a.qslots = v.sets[tsk::kSetIntSums];
     a.err = v.err;
-    if (plan.variant == TS_VARIANT_FUSED) return hip_status(tsk::launch_fused(a, plan.F, vec, grid, stream));
+    if (plan.variant == TS_VARIANT_FUSED)
+        return hip_status(tsk::launch_fused(a, plan.F, vec, tsk::kFusedProbs, grid, stream));
     return hip_status(tsk::launch_split(a, plan.F, vec, stream));
+}
+
+// Chunk size for the chunked sampling kernels of a (B, V) call: 4096 columns
+// while the call is small (latency-bound), else 8192 (their LDS holds one
+// transposed chunk, about 37 KiB at 8192); 0 if a row would need more than
+// kSlotStride chunks.
+int chunked_F(int64_t B, int64_t V) {
+    if (B * V <= (int64_t(1) << 21) && cdiv(V, 4096) <= tsk::kSlotStride) return 4;
+    if (cdiv(V, 8192) <= tsk::kSlotStride) return 8;
+    return 0;
 }
 
 }  // namespace
@@ -295,9 +312,79 @@ TS_API ts_status ts_sample(const float* probs, const float* uniforms, int64_t B,
     if (B > INT32_MAX) return TS_ERR_INVALID_ARGUMENT;
     if (overlaps(out_ids, B * K * 4, probs, B * V * 4) || overlaps(out_ids, B * K * 4, uniforms, B * K * 4))
         return TS_ERR_INVALID_ARGUMENT;
-    tsk::SampleArgs a{probs, uniforms, out_ids, B, V, K};
+    tsk::SampleArgs a{};
+    a.probs = probs;
+    a.uniforms = uniforms;
+    a.out_ids = out_ids;
+    a.B = B;
+    a.V = V;
+    a.K = K;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     const bool vec = aligned16(probs) && (V % 4 == 0);
-    return hip_status(tsk::launch_sample(a, vec, stream));
+    const int F = chunked_F(B, V);
+    if (F == 0) return hip_status(tsk::launch_sample_rows(a, vec, stream));
+    int64_t cap = 0;
+    ts_status st = resident_cap(3, F, vec, &cap);
+    if (st != TS_OK) return st;
+    a.nch = cdiv(V, 1024 * F);
+    a.items = B * a.nch;
+    if (a.nch > cap) return hip_status(tsk::launch_sample_rows(a, vec, stream));
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace* w = nullptr;
+    st = ws_get(stream, B, 0, &w);
+    if (st != TS_OK) return st;
+    const WsView v = ws_view(*w);
+    a.fslots = v.sets[tsk::kSetFloatSums];
+    a.qslots = v.sets[tsk::kSetIntSums];
+    a.err = v.err;
+    return hip_status(tsk::launch_sample_chunks(a, F, vec, fused_grid(a.items, a.nch, cap), stream));
+}
+
+TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, const float* uniforms, int64_t B,
+                                   int64_t V, int64_t K, float* probs_out, int32_t* out_ids, hipStream_t stream) {
+    if (!sizes_ok(B, V) || K < 0 || (K > 0 && B > (INT64_MAX / 8) / K)) return TS_ERR_INVALID_ARGUMENT;
+    if (B == 0) return TS_OK;
+    if (!logits || !temps || (K > 0 && (!uniforms || !out_ids))) return TS_ERR_INVALID_ARGUMENT;
+    const int64_t xbytes = B * V * 4, kbytes = B * K * 4;
+    if (probs_out) {
+        if (probs_out != logits && overlaps(probs_out, xbytes, logits, xbytes)) return TS_ERR_INVALID_ARGUMENT;
+        if (overlaps(probs_out, xbytes, temps, B * 4) || overlaps(probs_out, xbytes, uniforms, kbytes) ||
+            overlaps(probs_out, xbytes, out_ids, kbytes))
+            return TS_ERR_INVALID_ARGUMENT;
+    }
+    if (overlaps(out_ids, kbytes, logits, xbytes) || overlaps(out_ids, kbytes, temps, B * 4) ||
+        overlaps(out_ids, kbytes, uniforms, kbytes))
+        return TS_ERR_INVALID_ARGUMENT;
+    if (K == 0) return probs_out ? run_softmax(logits, temps, B, V, probs_out, TS_VARIANT_AUTO, 0, stream) : TS_OK;
+    const int F = chunked_F(B, V);
+    if (F == 0) return TS_ERR_INVALID_ARGUMENT;   // rows longer than kSlotStride * 8192 columns
+    const bool vec = aligned16(logits) && (V % 4 == 0) && (!probs_out || aligned16(probs_out));
+    const int mode = probs_out ? tsk::kFusedProbsIds : tsk::kFusedIds;
+    int64_t cap = 0;
+    ts_status st = resident_cap(mode, F, vec, &cap);
+    if (st != TS_OK) return st;
+    tsk::SoftmaxArgs a{};
+    a.logits = logits;
+    a.temps = temps;
+    a.out = probs_out;
+    a.B = B;
+    a.V = V;
+    a.nch = cdiv(V, 1024 * F);
+    a.items = B * a.nch;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    a.uniforms = uniforms;
+    a.out_ids = out_ids;
+    a.K = K;
+    if (a.nch > cap) return TS_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace* w = nullptr;
+    st = ws_get(stream, B, 0, &w);
+    if (st != TS_OK) return st;
+    const WsView v = ws_view(*w);
+    a.slots = v.sets[tsk::kSetPartials];
+    a.qslots = v.sets[tsk::kSetIntSums];
+    a.err = v.err;
+    return hip_status(tsk::launch_fused(a, F, vec, mode, fused_grid(a.items, a.nch, cap), stream));
 }
 
 TS_API ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream) {
