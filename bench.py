@@ -33,6 +33,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -350,6 +352,14 @@ def main(argv=None) -> int:
         extras["softmax_sample_with_probs_us_per_call"] = round(
             _elapsed_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids,
                                                                probs_out=ys[i % nsets]), 200), 3)
+        # the same masks applied from an allowed-id bitmask while the logits are read
+        # (finite logits everywhere, B * ceil(V/32) * 4 extra bytes read)
+        xm = torch.from_numpy(workloads.unmasked_logits(w)).to(dev)
+        bits = torch.from_numpy(workloads.make_allowed(w).view(np.int32).copy()).to(dev)
+        for i in range(10):
+            tsv.ts_softmax_masked(xm, ts[0], bits, out=ys[i % nsets])
+        extras["masked_bitmask_us_per_call"] = round(
+            _elapsed_us(torch, lambda i: tsv.ts_softmax_masked(xm, ts[0], bits, out=ys[i % nsets]), 200), 3)
         dp = torch.cuda.get_device_properties(dev)
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
                             "gcn_arch": getattr(dp, "gcnArchName", "")}

@@ -99,15 +99,32 @@ ts_status ts_softmax(const float* logits, const float* temps, int64_t B, int64_t
                      float* out, hipStream_t stream);
 
 /*
- * ts_softmax with the work split forced: `variant` is a ts_variant and
- * `chunk` the columns per workgroup (one of 1024, 2048, 4096, 8192, 16384 for
- * SPLIT and FUSED; ignored by ROWWISE; 0 = the table's choice). Same result
- * contract as ts_softmax. Meant for tests and tuning; a combination the
- * library cannot run (e.g. FUSED with more chunks per row than the GPU can
- * hold at once) returns TS_ERR_INVALID_ARGUMENT.
+ * ts_softmax with an allowed-token mask applied as the logits are read: the
+ * mask producers of the scope paragraph (allowed token ids, min-tokens,
+ * grammar) mark ids as not allowed, and such an id is treated exactly as a -inf
+ * logit, without a separate pass that writes -inf into the logits.
+ *
+ * allowed : [B, ceil(V / 32)] uint32, row-major. Id j of row b is allowed when
+ *           bit (j % 32) of allowed[b * ceil(V / 32) + j / 32] is 1; bits past
+ *           V are ignored. Must not be NULL (use ts_softmax for no mask) and
+ *           must not overlap out. Each row needs at least one allowed id with a
+ *           finite logit.
+ * Others  : as for ts_softmax. The result equals ts_softmax of the logits with
+ *           every disallowed id set to -inf, bit for bit.
  */
-ts_status ts_softmax_variant(const float* logits, const float* temps, int64_t B, int64_t V,
-                             float* out, int32_t variant, int32_t chunk, hipStream_t stream);
+ts_status ts_softmax_masked(const float* logits, const float* temps, const uint32_t* allowed, int64_t B,
+                            int64_t V, float* out, hipStream_t stream);
+
+/*
+ * ts_softmax (allowed == NULL) or ts_softmax_masked with the work split
+ * forced: `variant` is a ts_variant and `chunk` the columns per workgroup (one
+ * of 1024, 2048, 4096, 8192, 16384 for SPLIT and FUSED; ignored by ROWWISE;
+ * 0 = the table's choice). Same result contract. Meant for tests and tuning; a
+ * combination the library cannot run (e.g. FUSED with more chunks per row than
+ * it has slots for) returns TS_ERR_INVALID_ARGUMENT.
+ */
+ts_status ts_softmax_variant(const float* logits, const float* temps, const uint32_t* allowed, int64_t B,
+                             int64_t V, float* out, int32_t variant, int32_t chunk, hipStream_t stream);
 
 /*
  * The work split ts_softmax would use for (B, V) on the current device, for a
@@ -144,6 +161,7 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  * sampling row).
  *
  * logits, temps : as for ts_softmax.
+ * allowed       : NULL, or an allowed-id bitmask as for ts_softmax_masked.
  * uniforms      : [B, K] float32, as for ts_sample.
  * probs_out     : [B, V] float32 or NULL. If not NULL it receives the same
  *                 probabilities ts_softmax computes (probs_out == logits is
@@ -156,8 +174,9 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  *                 V above the limit. K == 0 reduces to ts_softmax (or a no-op
  *                 when probs_out is NULL).
  */
-ts_status ts_softmax_sample(const float* logits, const float* temps, const float* uniforms, int64_t B,
-                            int64_t V, int64_t K, float* probs_out, int32_t* out_ids, hipStream_t stream);
+ts_status ts_softmax_sample(const float* logits, const float* temps, const uint32_t* allowed,
+                            const float* uniforms, int64_t B, int64_t V, int64_t K, float* probs_out,
+                            int32_t* out_ids, hipStream_t stream);
 
 /*
  * Set aside the workspace for any later call with B <= max_B and

@@ -19,6 +19,9 @@ softmax when a chunk starts with -inf" (FreeToken pull request 654).
 * Masking (bug and fix paragraphs): masked logits are -inf; the result must be
   finite for every row that keeps at least one finite logit, and a masked
   entry's probability is exactly 0.
+* Mask producers (scope paragraph): allowed-token-ids, min-tokens and grammar
+  masks are what write -inf into the logits. softmax_masked_ref takes such a
+  mask as an allowed-id bitmask and applies it as -inf before the softmax.
 * Sampling (scope paragraph and the sampling row of the results table): the
   probabilities feed a draw of token ids, and every draw must be an allowed
   (finite-logit) id. The page does not spell out the draw rule; the reading
@@ -32,7 +35,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["softmax_ref", "sample_ref", "cdf_ref", "check_softmax_inputs"]
+__all__ = ["softmax_ref", "sample_ref", "cdf_ref", "check_softmax_inputs", "allowed_bits_to_bool",
+           "softmax_masked_ref"]
 
 
 def check_softmax_inputs(logits: np.ndarray, temps: np.ndarray) -> None:
@@ -125,3 +129,20 @@ def sample_ref(probs: np.ndarray, uniforms: np.ndarray) -> np.ndarray:
         j = np.searchsorted(c[b], target, side="right")   # first C[j] > target
         ids[b] = np.where(j < p.shape[1], j, nz[-1])
     return ids
+
+
+def allowed_bits_to_bool(allowed: np.ndarray, V: int) -> np.ndarray:
+    """[B, ceil(V/32)] uint32 words -> [B, V] bool: id j of row b is allowed
+    when bit (j % 32) of word j // 32 is 1. Written as the plain per-id rule."""
+    w = np.asarray(allowed)
+    if w.ndim != 2 or w.dtype != np.uint32 or w.shape[1] != (V + 31) // 32:
+        raise ValueError(f"allowed must be uint32 [B, {(V + 31) // 32}]")
+    j = np.arange(V)
+    return ((w[:, j // 32] >> (j % 32).astype(np.uint32)) & np.uint32(1)).astype(bool)
+
+
+def softmax_masked_ref(logits: np.ndarray, temps: np.ndarray, allowed: np.ndarray) -> np.ndarray:
+    """softmax_ref of the logits with every disallowed id set to -inf."""
+    x = np.asarray(logits)
+    keep = allowed_bits_to_bool(allowed, x.shape[1])
+    return softmax_ref(np.where(keep, x, np.float32(-np.inf)), temps)

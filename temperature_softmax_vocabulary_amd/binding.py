@@ -16,6 +16,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtsoftmax.so")
+# Same sources built without the -inf guard; loaded only by the tests that show
+# what the guard changes. Never used by the functions below.
+NOGUARD_LIB_PATH = os.path.join(_HERE, "libtsoftmax_noguard.so")
 
 TS_OK = 0
 TS_ERR_INVALID_ARGUMENT = 1
@@ -36,10 +39,11 @@ CHUNKS = (1024, 2048, 4096, 8192, 16384)
 _P, _I64, _I32, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
 SIGNATURES = {
     "ts_softmax": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
-    "ts_softmax_variant": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I32, _I32, _P]),
+    "ts_softmax_masked": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "ts_softmax_variant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _I32, _I32, _P]),
     "ts_plan": (ctypes.c_int, [_I64, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "ts_sample": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P]),
-    "ts_softmax_sample": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "ts_softmax_sample": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
     "ts_reserve": (ctypes.c_int, [_I64, _I64, _P]),
     "ts_device_errors": (ctypes.c_int, [_P, ctypes.POINTER(_U32)]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -57,18 +61,23 @@ class TsError(RuntimeError):
         self.status = status
 
 
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the C ABI and declare its signatures (raises if missing)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m temperature_softmax_vocabulary_amd.build`")
+    l = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(l, name)
+        fn.restype = res
+        fn.argtypes = args
+    return l
+
+
 def lib() -> ctypes.CDLL:
     """Load libtsoftmax.so from the package directory (raises if not built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built: run `python -m temperature_softmax_vocabulary_amd.build`")
-        l = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(l, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = l
+        _lib = load_library(LIB_PATH)
     return _lib
 
 
@@ -133,13 +142,35 @@ def ts_softmax(logits: torch.Tensor, temps: torch.Tensor, out: Optional[torch.Te
     return out
 
 
-def ts_softmax_variant(logits: torch.Tensor, temps: torch.Tensor, variant: int, chunk: int = 0,
-                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """ts_softmax with the work split forced (tests and tuning)."""
+def _allowed_arg(allowed, B, V, device):
+    if allowed is None:
+        return None
+    _need(allowed, "allowed", torch.int32 if allowed.dtype == torch.int32 else torch.uint32, 2)
+    if tuple(allowed.shape) != (B, (V + 31) // 32) or allowed.device != device:
+        raise ValueError(f"allowed must be [B, ceil(V/32)] = [{B}, {(V + 31) // 32}] 32-bit words on the device")
+    return allowed.data_ptr()
+
+
+def ts_softmax_masked(logits: torch.Tensor, temps: torch.Tensor, allowed: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ts_softmax with an allowed-id bitmask ([B, ceil(V/32)] int32/uint32; bit j%32
+    of word j//32 set = id j allowed) applied as -inf while the logits are read."""
     B, V, out = _softmax_args(logits, temps, out)
     with torch.cuda.device(logits.device):
-        _check(lib().ts_softmax_variant(logits.data_ptr(), temps.data_ptr(), B, V, out.data_ptr(),
-                                        int(variant), int(chunk), _stream_handle(logits.device, stream)))
+        _check(lib().ts_softmax_masked(logits.data_ptr(), temps.data_ptr(), _allowed_arg(allowed, B, V, logits.device),
+                                       B, V, out.data_ptr(), _stream_handle(logits.device, stream)))
+    return out
+
+
+def ts_softmax_variant(logits: torch.Tensor, temps: torch.Tensor, variant: int, chunk: int = 0,
+                       out: Optional[torch.Tensor] = None, stream=None,
+                       allowed: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ts_softmax (or ts_softmax_masked) with the work split forced (tests and tuning)."""
+    B, V, out = _softmax_args(logits, temps, out)
+    with torch.cuda.device(logits.device):
+        _check(lib().ts_softmax_variant(logits.data_ptr(), temps.data_ptr(), _allowed_arg(allowed, B, V, logits.device),
+                                        B, V, out.data_ptr(), int(variant), int(chunk),
+                                        _stream_handle(logits.device, stream)))
     return out
 
 
@@ -175,7 +206,7 @@ def ts_sample(probs: torch.Tensor, uniforms: torch.Tensor, out_ids: Optional[tor
 
 def ts_softmax_sample(logits: torch.Tensor, temps: torch.Tensor, uniforms: torch.Tensor,
                       out_ids: Optional[torch.Tensor] = None, probs_out=False,
-                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                      stream=None, allowed: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Softmax and inverse-CDF draw in one pass over the logits.
 
     Returns (ids [B, K] int32, probs [B, V] or None). probs_out: False (do not
@@ -199,7 +230,8 @@ def ts_softmax_sample(logits: torch.Tensor, temps: torch.Tensor, uniforms: torch
     else:
         _, _, probs = _softmax_args(logits, temps, probs_out)
     with torch.cuda.device(logits.device):
-        _check(lib().ts_softmax_sample(logits.data_ptr(), temps.data_ptr(), uniforms.data_ptr(), B, V, K,
+        _check(lib().ts_softmax_sample(logits.data_ptr(), temps.data_ptr(), _allowed_arg(allowed, B, V, logits.device),
+                                       uniforms.data_ptr(), B, V, K,
                                        probs.data_ptr() if probs is not None else None, out_ids.data_ptr(),
                                        _stream_handle(logits.device, stream)))
     return out_ids, probs

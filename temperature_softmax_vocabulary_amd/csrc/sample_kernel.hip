@@ -218,7 +218,7 @@ __global__ __launch_bounds__(CT) void ts_sample_chunks(SampleArgs a) {
         fsum = block_reduce<SumOp, CW>(fsum, redf);
         if (lane < kWave) {
             const unsigned long long tf = next_tag(own_f);
-            publish(fs, c, a.nch, tf, __float_as_uint(fsum));
+            publish(fs, c, a.nch, tf, __float_as_uint(fsum) & 0x7fffffffu);   // a sum of positives
             unsigned long long v[kSlotsPerLane];
             wait_row(fs, a.nch, tf, 0ull, v, a.spin_limit, a.err);
             float tot = 0.0f;

@@ -33,6 +33,10 @@ constexpr int NW = NT / kWave;
 
 __device__ __forceinline__ float2 load_partial(const float2* p) { return *p; }
 
+__device__ __forceinline__ const uint32_t* mask_row(const SoftmaxArgs& a, int64_t row) {
+    return a.allowed ? a.allowed + row * a.mwords : nullptr;
+}
+
 // ---------------------------------------------------------------------------
 // split, kernel 1: one workgroup per (row, chunk) -> (pm, pl)
 // ---------------------------------------------------------------------------
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(NT) void ts_split_partials(SoftmaxArgs a) {
     const float k = exp2_scale(a.temps[row]);
 
     float x[4 * F];
-    load_chunk<NT, F, VEC, false>(a.logits + row * a.V, c * C, a.V, x);
+    load_chunk<NT, F, VEC, false>(a.logits + row * a.V, c * C, a.V, x, kNegInf, mask_row(a, row));
 
     float m = kNegInf;
 #pragma unroll
@@ -71,7 +75,7 @@ __device__ __forceinline__ void combine_row(const float2* __restrict__ part, int
     float l = 0.0f;
     for (int64_t i = threadIdx.x; i < nch; i += NT) {
         const float2 p = load_partial(part + i);
-        l += (p.x == kNegInf) ? 0.0f : p.y * exp2_hw((p.x - gsh) * k);
+        l += masked_term(p.x, p.y * exp2_hw((p.x - gsh) * k));
     }
     const float gl = block_reduce<SumOp, NW>(l, red);
     r = 1.0f / gl;
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
     const float k = exp2_scale(a.temps[row]);
 
     float x[4 * F];
-    load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x);   // last use of logits
+    load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x, kNegInf, mask_row(a, row));   // last use of logits
 
     float gsh, r;
     combine_row(a.part + row * a.nch, a.nch, k, red, gsh, r);
@@ -119,7 +123,7 @@ template <int F, int MODE>
 struct FusedOcc {
     // registers hold the current and the next chunk (8 F floats per lane);
     // the sampling modes need about 60 more for the second exchange
-    static constexpr int probs_only = F <= 4 ? 8 : (F == 8 ? 4 : 2);
+    static constexpr int probs_only = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
     static constexpr int waves_per_eu = MODE == kFusedProbs ? probs_only : (F <= 2 ? 4 : (F == 4 ? 3 : 2));
 };
 
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
     unsigned long long own = 0, next_own = 0, own_q = 0, next_own_q = 0;
     {
         const int64_t row = item / a.nch, c = item - row * a.nch;
-        load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x);
+        load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x, kNegInf, mask_row(a, row));
         if (lane == 0) {
             own = slot_load(a.slots + row * kSlotStride + c);
             if (SAMPLE) own_q = slot_load(a.qslots + row * kSlotStride + c);
@@ -175,14 +179,16 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
 
         const unsigned long long tag = next_tag(own);   // wave-uniform, all lanes
         if (lane < kWave)
-            publish(rs, c, a.nch,
-                    tag, (static_cast<unsigned long long>(__float_as_uint(pl)) << 32) | __float_as_uint(pm));
+            // pl >= 0; clearing its sign bit keeps a NaN (possible only outside the
+            // method's domain) from reaching the tag bit
+            publish(rs, c, a.nch, tag,
+                    (static_cast<unsigned long long>(__float_as_uint(pl) & 0x7fffffffu) << 32) | __float_as_uint(pm));
 
         // prefetch the next item (a later row: gridDim.x >= nch)
         const int64_t nitem = item + gridDim.x;
         if (nitem < a.items) {
             const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
-            load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx);
+            load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx, kNegInf, mask_row(a, nr));
             if (lane == 0) {
                 next_own = slot_load(a.slots + nr * kSlotStride + nc);
                 if (SAMPLE) next_own_q = slot_load(a.qslots + nr * kSlotStride + nc);
@@ -204,10 +210,10 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
             for (int j = 0; j < kSlotsPerLane; ++j) {
                 const float vm = __uint_as_float(static_cast<uint32_t>(v[j]));
                 const float vl = __uint_as_float(static_cast<uint32_t>(v[j] >> 32));
-                ll += (vm == kNegInf) ? 0.0f : vl * exp2_hw((vm - gsh) * k);
+                ll += masked_term(vm, vl * exp2_hw((vm - gsh) * k));
             }
             const float gl = wave_reduce<SumOp>(ll);
-            if (lane == 0) chunk_scale = (pm == kNegInf) ? 0.0f : exp2_hw((pm - gsh) * k) * (1.0f / gl);
+            if (lane == 0) chunk_scale = masked_term(pm, exp2_hw((pm - gsh) * k) * (1.0f / gl));
         }
         __syncthreads();
         const float scale = chunk_scale;
@@ -250,11 +256,12 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
                     for (int64_t kk = lane; kk < a.K; kk += NT) idrow[kk] = -1;
             } else {
                 const float* xr = a.logits + row * a.V;
+                const uint32_t* mrow = mask_row(a, row);
                 const int64_t c0 = c * C;
                 const int64_t V = a.V;
                 // p = exp2((x - sh) k) * scale, as computed above for x[]
                 auto fetch = [=](int j, int o, float (&v)[4]) {
-                    load_group4<NT>(xr, c0, V, j, o, kNegInf, v);
+                    load_group4<NT>(xr, c0, V, j, o, kNegInf, v, mrow);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = exp2_hw((v[e] - sh) * k) * scale;
                 };
@@ -282,7 +289,7 @@ __global__ __launch_bounds__(RT) void ts_rowwise_resident(SoftmaxArgs a) {
     const int64_t row = blockIdx.x;
     const float k = exp2_scale(a.temps[row]);
     float x[4 * F];
-    load_chunk<RT, F, VEC, true>(a.logits + row * a.V, 0, a.V, x);
+    load_chunk<RT, F, VEC, true>(a.logits + row * a.V, 0, a.V, x, kNegInf, mask_row(a, row));
     float m = kNegInf;
 #pragma unroll
     for (int i = 0; i < 4 * F; ++i) m = fmaxf(m, x[i]);
@@ -313,11 +320,12 @@ __global__ __launch_bounds__(RT) void ts_rowwise_stream(SoftmaxArgs a) {
     const float k = exp2_scale(a.temps[row]);
     const float* xr = a.logits + row * a.V;
     float* yr = a.out + row * a.V;
+    const uint32_t* mrow = mask_row(a, row);
 
     float m = kNegInf, l = 0.0f;
     for (int64_t c0 = 0; c0 < a.V; c0 += TILE) {
         float x[4 * U];
-        load_chunk<RT, U, VEC, false>(xr, c0, a.V, x);
+        load_chunk<RT, U, VEC, false>(xr, c0, a.V, x, kNegInf, mrow);
         float bm = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4 * U; ++i) bm = fmaxf(bm, x[i]);
@@ -331,11 +339,11 @@ __global__ __launch_bounds__(RT) void ts_rowwise_stream(SoftmaxArgs a) {
         m = nm;
     }
     const float gsh = guarded_shift(block_reduce<MaxOp, RW>(m, red));
-    const float mine = (m == kNegInf) ? 0.0f : l * exp2_hw((m - gsh) * k);
+    const float mine = masked_term(m, l * exp2_hw((m - gsh) * k));
     const float r = 1.0f / block_reduce<SumOp, RW>(mine, red);
     for (int64_t c0 = 0; c0 < a.V; c0 += TILE) {
         float x[4 * U];
-        load_chunk<RT, U, VEC, true>(xr, c0, a.V, x);
+        load_chunk<RT, U, VEC, true>(xr, c0, a.V, x, kNegInf, mrow);
 #pragma unroll
         for (int i = 0; i < 4 * U; ++i) x[i] = exp2_hw((x[i] - gsh) * k) * r;
         store_chunk<RT, U, VEC, true>(yr, c0, a.V, x);

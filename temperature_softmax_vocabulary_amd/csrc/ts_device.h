@@ -31,8 +31,23 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // The fix (fix paragraph): while a max is still -inf the shift is 0, so an all
 // -inf block contributes exp2(-inf) = 0 instead of exp2(-inf - -inf) = NaN.
 // For a finite max this is the plain max: a pure select, no change to the
-// arithmetic of rows without -inf.
-__device__ __forceinline__ float guarded_shift(float m) { return m == kNegInf ? 0.0f : m; }
+// arithmetic of rows without -inf. A library built with TS_NO_INF_GUARD drops
+// the selects (the arithmetic before the fix); it exists only so that tests
+// can show both that finite rows are bitwise unchanged by the guard (A/B list
+// of the page) and that masked chunk starts give NaN without it (bug paragraph).
+#ifdef TS_NO_INF_GUARD
+constexpr bool kInfGuard = false;
+#else
+constexpr bool kInfGuard = true;
+#endif
+
+__device__ __forceinline__ float guarded_shift(float m) { return (kInfGuard && m == kNegInf) ? 0.0f : m; }
+
+// A chunk (or lane) whose max is -inf adds exactly 0 to a rescaled sum, even
+// when the row's own max is -inf too; `term` is the rescaled value otherwise.
+__device__ __forceinline__ float masked_term(float m, float term) {
+    return (kInfGuard && m == kNegInf) ? 0.0f : term;
+}
 
 // ---------------------------------------------------------------------------
 // Wave64 reductions with DPP. Steps: two quad permutes (sum of 4 lanes), half
@@ -94,10 +109,22 @@ __device__ __forceinline__ float block_reduce(float v, float* lds) {
 // checked 4-byte loads per group. Columns at or past V read as `fill` (-inf
 // for logits: they add nothing to a max or to a sum of exponentials).
 // ---------------------------------------------------------------------------
+// allowed-id bitmask of one row: bit (j % 32) of word j / 32, 1 = allowed. A
+// lane's 4 columns of a group share one word (4 divides 32), so the mask costs
+// one 4-byte load per group.
+__device__ __forceinline__ void apply_allowed(const uint32_t* __restrict__ mrow, int64_t col, float (&v)[4]) {
+    const uint32_t bits = mrow[col >> 5] >> (col & 31);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (!((bits >> e) & 1u)) v[e] = kNegInf;
+}
+
 template <int NT, int F, bool VEC, bool NT_LOAD>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t c0, int64_t V,
-                                           float (&x)[4 * F], float fill = kNegInf) {
+                                           float (&x)[4 * F], float fill = kNegInf,
+                                           const uint32_t* __restrict__ mrow = nullptr) {
     const int t = threadIdx.x;
+    // every load is issued before any value is used
     if constexpr (VEC) {
 #pragma unroll
         for (int j = 0; j < F; ++j) {
@@ -124,6 +151,19 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_
                 x[4 * j + e] = v;
             }
         }
+    }
+    if (mrow) {
+        uint32_t w[F];
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+            w[j] = (col < V) ? (mrow[col >> 5] >> (col & 31)) : 0xFu;
+        }
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!((w[j] >> e) & 1u)) x[4 * j + e] = kNegInf;
     }
 }
 

@@ -31,6 +31,8 @@ constexpr int64_t kRowwiseResidentMaxV = 16384;
 struct SoftmaxArgs {
     const float* logits;   // [B, V]
     const float* temps;    // [B]
+    const uint32_t* allowed;  // [B, mwords] allowed-id bitmask, or null (no mask)
+    int64_t mwords;        // ceil(V / 32)
     float* out;            // [B, V]
     int64_t B;
     int64_t V;

@@ -194,10 +194,11 @@ __device__ __forceinline__ void resolve_chunk(const float (&p)[4 * F], unsigned 
 // same instructions that produced them in registers (fused softmax-and-draw).
 template <int NT>
 __device__ __forceinline__ void load_group4(const float* __restrict__ row, int64_t c0, int64_t V, int j, int o,
-                                            float fill, float (&v)[4]) {
+                                            float fill, float (&v)[4], const uint32_t* __restrict__ mrow = nullptr) {
     const int64_t col = c0 + (static_cast<int64_t>(j) * NT + o) * 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (col + e < V) ? row[col + e] : fill;
+    if (mrow && col < V) apply_allowed(mrow, col, v);
 }
 
 }  // namespace tsk

@@ -199,14 +199,17 @@ int64_t fused_grid(int64_t items, int64_t nch, int64_t cap) {
     return g;
 }
 
-ts_status run_softmax(const float* logits, const float* temps, int64_t B, int64_t V, float* out,
-                      int variant, int chunk, hipStream_t stream) {
+int64_t mask_words(int64_t V) { return (V + 31) / 32; }
+
+ts_status run_softmax(const float* logits, const float* temps, const uint32_t* allowed, int64_t B, int64_t V,
+                      float* out, int variant, int chunk, hipStream_t stream) {
     if (!sizes_ok(B, V)) return TS_ERR_INVALID_ARGUMENT;
     if (B == 0) return TS_OK;
     if (!logits || !temps || !out) return TS_ERR_INVALID_ARGUMENT;
     const int64_t xbytes = B * V * 4;
     if (out != logits && overlaps(out, xbytes, logits, xbytes)) return TS_ERR_INVALID_ARGUMENT;
     if (overlaps(out, xbytes, temps, B * 4)) return TS_ERR_INVALID_ARGUMENT;
+    if (allowed && overlaps(out, xbytes, allowed, B * mask_words(V) * 4)) return TS_ERR_INVALID_ARGUMENT;
     if (variant < TS_VARIANT_AUTO || variant > TS_VARIANT_FUSED) return TS_ERR_INVALID_ARGUMENT;
     int F = 0;
     if (chunk != 0) {
@@ -233,6 +236,8 @@ ts_status run_softmax(const float* logits, const float* temps, int64_t B, int64_
     tsk::SoftmaxArgs a{};
     a.logits = logits;
     a.temps = temps;
+    a.allowed = allowed;
+    a.mwords = mask_words(V);
     a.out = out;
     a.B = B;
     a.V = V;
@@ -286,12 +291,18 @@ int chunked_F(int64_t B, int64_t V) {
 
 TS_API ts_status ts_softmax(const float* logits, const float* temps, int64_t B, int64_t V, float* out,
                             hipStream_t stream) {
-    return run_softmax(logits, temps, B, V, out, TS_VARIANT_AUTO, 0, stream);
+    return run_softmax(logits, temps, nullptr, B, V, out, TS_VARIANT_AUTO, 0, stream);
 }
 
-TS_API ts_status ts_softmax_variant(const float* logits, const float* temps, int64_t B, int64_t V,
-                                    float* out, int32_t variant, int32_t chunk, hipStream_t stream) {
-    return run_softmax(logits, temps, B, V, out, variant, chunk, stream);
+TS_API ts_status ts_softmax_masked(const float* logits, const float* temps, const uint32_t* allowed, int64_t B,
+                                   int64_t V, float* out, hipStream_t stream) {
+    if (B > 0 && !allowed) return TS_ERR_INVALID_ARGUMENT;
+    return run_softmax(logits, temps, allowed, B, V, out, TS_VARIANT_AUTO, 0, stream);
+}
+
+TS_API ts_status ts_softmax_variant(const float* logits, const float* temps, const uint32_t* allowed, int64_t B,
+                                    int64_t V, float* out, int32_t variant, int32_t chunk, hipStream_t stream) {
+    return run_softmax(logits, temps, allowed, B, V, out, variant, chunk, stream);
 }
 
 TS_API ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk) {
@@ -340,8 +351,9 @@ TS_API ts_status ts_sample(const float* probs, const float* uniforms, int64_t B,
     return hip_status(tsk::launch_sample_chunks(a, F, vec, fused_grid(a.items, a.nch, cap), stream));
 }
 
-TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, const float* uniforms, int64_t B,
-                                   int64_t V, int64_t K, float* probs_out, int32_t* out_ids, hipStream_t stream) {
+TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, const uint32_t* allowed,
+                                   const float* uniforms, int64_t B, int64_t V, int64_t K, float* probs_out,
+                                   int32_t* out_ids, hipStream_t stream) {
     if (!sizes_ok(B, V) || K < 0 || (K > 0 && B > (INT64_MAX / 8) / K)) return TS_ERR_INVALID_ARGUMENT;
     if (B == 0) return TS_OK;
     if (!logits || !temps || (K > 0 && (!uniforms || !out_ids))) return TS_ERR_INVALID_ARGUMENT;
@@ -355,7 +367,11 @@ TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, cons
     if (overlaps(out_ids, kbytes, logits, xbytes) || overlaps(out_ids, kbytes, temps, B * 4) ||
         overlaps(out_ids, kbytes, uniforms, kbytes))
         return TS_ERR_INVALID_ARGUMENT;
-    if (K == 0) return probs_out ? run_softmax(logits, temps, B, V, probs_out, TS_VARIANT_AUTO, 0, stream) : TS_OK;
+    const int64_t mbytes = B * mask_words(V) * 4;
+    if (allowed && (overlaps(out_ids, kbytes, allowed, mbytes) || (probs_out && overlaps(probs_out, xbytes, allowed, mbytes))))
+        return TS_ERR_INVALID_ARGUMENT;
+    if (K == 0)
+        return probs_out ? run_softmax(logits, temps, allowed, B, V, probs_out, TS_VARIANT_AUTO, 0, stream) : TS_OK;
     const int F = chunked_F(B, V);
     if (F == 0) return TS_ERR_INVALID_ARGUMENT;   // rows longer than kSlotStride * 8192 columns
     const bool vec = aligned16(logits) && (V % 4 == 0) && (!probs_out || aligned16(probs_out));
@@ -366,6 +382,8 @@ TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, cons
     tsk::SoftmaxArgs a{};
     a.logits = logits;
     a.temps = temps;
+    a.allowed = allowed;
+    a.mwords = mask_words(V);
     a.out = probs_out;
     a.B = B;
     a.V = V;

@@ -138,3 +138,28 @@ def make(B: int, V: int, masks: str = "none", K: int = 64, seed: Optional[int] =
 def make_config(name: str, K: int = 64) -> Workload:
     c = CONFIGS[name]
     return make(c["B"], c["V"], c["masks"], K=K, name=name)
+
+
+def pack_allowed(keep: np.ndarray) -> np.ndarray:
+    """[B, V] bool -> [B, ceil(V/32)] uint32, bit (j % 32) of word j // 32 = keep[:, j]."""
+    B, V = keep.shape
+    W = (V + 31) // 32
+    pad = np.zeros((B, W * 32), dtype=bool)
+    pad[:, :V] = keep
+    bits = pad.reshape(B, W, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)
+    return bits.sum(axis=2).astype(np.uint32)
+
+
+def make_allowed(w: Workload) -> np.ndarray:
+    """The workload's -inf pattern as an allowed-id bitmask (1 = allowed)."""
+    return pack_allowed(np.isfinite(w.logits))
+
+
+def unmasked_logits(w: Workload, seed: int = 0) -> np.ndarray:
+    """The workload's logits with every -inf replaced by a fresh finite draw,
+    so that the same pattern can be applied through a bitmask instead."""
+    rng = np.random.Generator(np.random.PCG64(w.seed ^ 0x5EED ^ seed))
+    x = w.logits.copy()
+    bad = ~np.isfinite(x)
+    x[bad] = rng.standard_normal(int(bad.sum()), dtype=np.float32) * np.float32(4.0)
+    return x

@@ -71,9 +71,18 @@ def test_softmax_rejects_partial_overlap_but_not_exact_alias_check(L):
 
 
 def test_softmax_variant_rejects_bad_variant_or_chunk(L):
-    assert L.ts_softmax_variant(FAKE_A, FAKE_B, 2, 100, FAKE_A, 7, 0, None) == INVALID
-    assert L.ts_softmax_variant(FAKE_A, FAKE_B, 2, 100, FAKE_A, 1, 3000, None) == INVALID
-    assert L.ts_softmax_variant(FAKE_A, FAKE_B, 2, 100, FAKE_A, 1, 32768, None) == INVALID
+    assert L.ts_softmax_variant(FAKE_A, FAKE_B, None, 2, 100, FAKE_A, 7, 0, None) == INVALID
+    assert L.ts_softmax_variant(FAKE_A, FAKE_B, None, 2, 100, FAKE_A, 1, 3000, None) == INVALID
+    assert L.ts_softmax_variant(FAKE_A, FAKE_B, None, 2, 100, FAKE_A, 1, 32768, None) == INVALID
+
+
+def test_masked_argument_checks(L):
+    # the mask is required, and may not overlap the output
+    assert L.ts_softmax_masked(FAKE_A, FAKE_B, None, 2, 100, FAKE_A + (1 << 30), None) == INVALID
+    assert L.ts_softmax_masked(FAKE_A, FAKE_B, FAKE_A + (1 << 30) + 64, 2, 100, FAKE_A + (1 << 30), None) == INVALID
+    assert L.ts_softmax_masked(None, None, None, 0, 100, None, None) == binding.TS_OK
+    assert L.ts_softmax_sample(FAKE_A, FAKE_B, FAKE_A + (1 << 31), FAKE_B + 64, 2, 100, 4, None,
+                               FAKE_A + (1 << 31) + 4, None) == INVALID
 
 
 def test_sample_argument_checks(L):

@@ -278,3 +278,52 @@ def test_cdf_is_inclusive_prefix_sum():
     p = np.array([[0.5, 0.25, 0.25]])
     assert cdf_ref(p).tolist() == [[0.5, 0.75, 1.0]]
     assert math.isclose(cdf_ref(np.ones((1, 10)) / 10)[0, -1], 1.0)
+
+
+# ----------------------------------------------------------------------------
+# allowed-id bitmask (mask producers of the scope paragraph)
+# ----------------------------------------------------------------------------
+
+def test_bitmask_bit_order_single_allowed_id_is_one_hot():
+    # one allowed id at a word boundary, inside a word, at the row end: the
+    # result must be one-hot exactly there (catches bit order / word index slips)
+    from oracle import softmax_masked_ref
+    V = 100
+    for j in (0, 1, 31, 32, 33, 63, 64, 99):
+        bits = np.zeros((1, (V + 31) // 32), np.uint32)
+        bits[0, j // 32] = np.uint32(1) << np.uint32(j % 32)
+        x = np.random.default_rng(j).standard_normal((1, V)).astype(np.float32)
+        p = softmax_masked_ref(x, np.ones(1, np.float32), bits)
+        assert p[0, j] == 1.0 and np.count_nonzero(p) == 1, j
+
+
+def test_bitmask_all_ones_and_equivalence_with_pre_masked_logits():
+    from oracle import softmax_masked_ref
+    w = workloads.make(6, 5003, "quarters", seed=21)
+    ones = np.full((6, (5003 + 31) // 32), 0xFFFFFFFF, np.uint32)
+    finite = np.where(np.isfinite(w.logits), w.logits, np.float32(0.0))
+    np.testing.assert_array_equal(softmax_masked_ref(finite, w.temps, ones), softmax_ref(finite, w.temps))
+    # the workload's -inf pattern as bits, applied to different finite values there
+    bits = workloads.make_allowed(w)
+    x = workloads.unmasked_logits(w)
+    assert np.all(np.isfinite(x)) and np.array_equal(x[np.isfinite(w.logits)], w.logits[np.isfinite(w.logits)])
+    np.testing.assert_array_equal(softmax_masked_ref(x, w.temps, bits), softmax_ref(w.logits, w.temps))
+
+
+def test_bitmask_two_allowed_ids_logistic():
+    from oracle import softmax_masked_ref
+    V = 70
+    x = np.random.default_rng(2).standard_normal((1, V)).astype(np.float32) * 4
+    keep = np.zeros((1, V), bool)
+    keep[0, [5, 66]] = True
+    p = softmax_masked_ref(x, np.array([0.7], np.float32), workloads.pack_allowed(keep))
+    pa = scipy.special.expit((float(x[0, 5]) - float(x[0, 66])) / float(np.float32(0.7)))
+    assert abs(p[0, 5] - pa) <= 1e-15 and abs(p[0, 66] - (1 - pa)) <= 1e-15
+
+
+def test_pack_allowed_round_trips():
+    from oracle import allowed_bits_to_bool
+    keep = np.random.default_rng(3).random((4, 1000)) < 0.3
+    assert np.array_equal(allowed_bits_to_bool(workloads.pack_allowed(keep), 1000), keep)
+    with pytest.raises(ValueError):
+        allowed_bits_to_bool(np.zeros((4, 31), np.uint32), 1000)
