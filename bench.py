@@ -205,12 +205,19 @@ def main(argv=None) -> int:
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-extras", action="store_true", help="skip the hot/copy/sample side measurements")
+    ap.add_argument("--extras", choices=("all", "copy", "none"), default="all",
+                    help="side measurements after the timed region: all, only the copy "
+                         "(the counter runs' calibration), or none")
+    ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--profile-command", default="python3 bench.py --steps 200 --warmup 20 --no-cpu-baseline",
                     help="the profiled command, recorded in the summaries")
+    ap.add_argument("--summary-tag", default=None,
+                    help="file tag of a trace summary (default: the profiled kernel's)")
     args = ap.parse_args(argv)
+    if args.no_extras:
+        args.extras = "none"
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -228,7 +235,8 @@ def main(argv=None) -> int:
             raise SystemExit("--summarize-* needs --variant and --chunk of the profiled plan")
         name, tag = _kernel_names(tsv, (args.variant, args.chunk))
         if args.summarize_trace:
-            print(summarize_trace(args.summarize_trace, args.workload, name, tag, args.profile_command))
+            print(summarize_trace(args.summarize_trace, args.workload, name, args.summary_tag or tag,
+                                  args.profile_command))
         if args.summarize_counters:
             print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
                                      name, tag, args.profile_command))
@@ -297,15 +305,10 @@ def main(argv=None) -> int:
         "outputs_sane": sane,
     }
 
-    if not args.no_extras:
-        extras = {}
-        # hot: the same buffers every call (how the page timed, graph replays of one input)
-        def hot(i):
-            step(0)
-        for i in range(20):
-            hot(i)
-        extras["hot_us_per_call"] = round(_elapsed_us(torch, hot, 200), 3)
-        # same bytes through a plain streaming copy, cold (practical ceiling)
+    extras = {}
+    if args.extras in ("all", "copy"):
+        # same bytes through a plain streaming copy, cold (practical ceiling,
+        # and the byte-counter calibration of the profile runs)
         def cp(i):
             j = i % nsets
             tsv.ts_copy_f32(xs[j], ys[j])
@@ -315,6 +318,13 @@ def main(argv=None) -> int:
         extras["copy_us_per_call"] = round(cus, 3)
         extras["copy_GBps"] = round(bytes_per_call / cus / 1e3, 1)
         extras["softmax_over_copy"] = round(cus / us, 4)
+    if args.extras == "all":
+        # hot: the same buffers every call (how the page timed, graph replays of one input)
+        def hot(i):
+            step(0)
+        for i in range(20):
+            hot(i)
+        extras["hot_us_per_call"] = round(_elapsed_us(torch, hot, 200), 3)
         # graph replay of the same rotating calls (launch gaps removed)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -354,15 +364,23 @@ def main(argv=None) -> int:
                                                                probs_out=ys[i % nsets]), 200), 3)
         # the same masks applied from an allowed-id bitmask while the logits are read
         # (finite logits everywhere, B * ceil(V/32) * 4 extra bytes read)
-        xm = torch.from_numpy(workloads.unmasked_logits(w)).to(dev)
-        bits = torch.from_numpy(workloads.make_allowed(w).view(np.int32).copy()).to(dev)
+        # (cold like the timed region: the logit and mask buffers rotate too)
+        xm_host = workloads.unmasked_logits(w)
+        bits_host = workloads.make_allowed(w).view(np.int32)
+        xms = [torch.from_numpy(xm_host).to(dev) for _ in range(nsets)]
+        bitss = [torch.from_numpy(bits_host.copy()).to(dev) for _ in range(nsets)]
+
+        def masked(i):
+            j = i % nsets
+            tsv.ts_softmax_masked(xms[j], ts[j], bitss[j], out=ys[j])
         for i in range(10):
-            tsv.ts_softmax_masked(xm, ts[0], bits, out=ys[i % nsets])
-        extras["masked_bitmask_us_per_call"] = round(
-            _elapsed_us(torch, lambda i: tsv.ts_softmax_masked(xm, ts[0], bits, out=ys[i % nsets]), 200), 3)
+            masked(i)
+        extras["masked_bitmask_us_per_call"] = round(_elapsed_us(torch, masked, 200), 3)
+        del xms, bitss
         dp = torch.cuda.get_device_properties(dev)
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
                             "gcn_arch": getattr(dp, "gcnArchName", "")}
+    if extras:
         extras["kernel_source_sha256"] = kernel_source_hash()
         result["extras"] = extras
 
@@ -376,7 +394,7 @@ def _kernel_names(tsv, plan):
     """(kernel-name substring as rocprofv3 prints it, file tag) for a plan."""
     v, c = plan
     if v == tsv.TS_VARIANT_FUSED:
-        return f"ts_fused<{c // 1024}, true>", f"ts_fused_c{c}"
+        return f"ts_fused<{c // 1024}, true, 0>", f"ts_fused_c{c}"
     if v == tsv.TS_VARIANT_SPLIT:
         return f"ts_split_finalize_write<{c // 1024}, true>", f"ts_split_c{c}"
     return "ts_rowwise", "ts_rowwise"
