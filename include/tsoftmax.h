@@ -143,9 +143,13 @@ ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
  * out_ids  : [B, K] int32. For each (b, k): with C the row's inclusive
  *            prefix sums and target = u * C[V-1], the smallest id j with
  *            C[j] > target; for u = 1 the last id with a positive entry.
- *            The prefix sums are formed exactly, in 64-bit fixed point at a
- *            per-row power-of-two scale, so the id is always one with a
- *            positive probability. A row with no positive entry gives -1.
+ *            Prefix sums are integers: inside a column chunk, the entries in
+ *            64-bit fixed point at a power-of-two scale (exact); across chunks,
+ *            the chunks' float sums at one power-of-two scale per row, so a
+ *            chunk boundary can sit about 1e-7 of the row total away from the
+ *            exact one (rows of more than 2,097,152 ids: one exact sum over
+ *            the row). The id is always one with a positive entry. A row with
+ *            no positive entry (or a sum that is not finite) gives -1.
  * Errors   : TS_ERR_INVALID_ARGUMENT for B < 0, K < 0, V < 1,
  *            V > INT32_MAX, a NULL pointer when B*K > 0, or out_ids overlapping
  *            probs or uniforms. B == 0 or K == 0 is a no-op.
@@ -167,8 +171,9 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  *                 probabilities ts_softmax computes (probs_out == logits is
  *                 allowed); if NULL the probabilities are never written.
  * out_ids       : [B, K] int32. The inverse-CDF rule of ts_sample, applied to
- *                 the probabilities in 64-bit fixed point at the fixed scale
- *                 2^60 (they sum to 1); -1 for a row with no finite logit.
+ *                 the probabilities with the same chunked integer prefix sums;
+ *                 every id drawn has a finite logit (and an allowed bit); -1
+ *                 for a row with none.
  * Limits        : V <= 2,097,152 (256 chunks of 8192 columns per row).
  * Errors        : as ts_softmax and ts_sample; TS_ERR_INVALID_ARGUMENT also for
  *                 V above the limit. K == 0 reduces to ts_softmax (or a no-op

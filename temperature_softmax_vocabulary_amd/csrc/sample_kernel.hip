@@ -8,25 +8,19 @@
 // and the row's inclusive prefix sums C, the id is the smallest j with
 // C[j] > u * C[V-1].
 //
-// Exactness: the prefix sums are formed in 64-bit fixed point. Each entry p > 0
-// becomes q = rint(p * 2^s), where 2^s is a per-row power of two chosen from
-// the row's float sum so that sum(q) < 2^62. Scaling by a power of two is
-// exact, integer addition is associative, and an entry that is not > 0 gives
-// q = 0; with Q[j] the integer prefix sums and T = min(floor(u * Q[V-1]),
-// Q[V-1] - 1), the id is the smallest j with Q[j] > T. That j always has
-// q[j] >= 1, so a masked (zero-probability) id can never be drawn, whatever
-// the order in which lanes add. Rounding is <= 0.5 * 2^-s per entry, i.e.
-// about 2^-62 of the row total.
-//
 // Two kernels:
 //  ts_sample_chunks: (row, chunk) items over a persistent grid, one read of the
-//    probabilities. Each chunk's positive-entry float sum and then its exact
-//    integer sum travel between the row's workgroups through the tagged slots
-//    of ts_exchange.h; the chunk that holds a target resolves it. Used while a
-//    row has at most kSlotStride chunks.
+//    probabilities. Each chunk's positive-entry float sum travels between the
+//    row's workgroups through the tagged slots of ts_exchange.h; every
+//    workgroup turns the sums into the row's integer chunk ranges, and the
+//    chunk whose range holds a target resolves it in its own exact fixed point
+//    (ts_sample_device.h). Used while a row has at most kSlotStride chunks.
 //  ts_sample_rows: one workgroup per row, three sweeps over the row (float
 //    sum for the scale, exact integer total, then a tile walk with an integer
-//    carry). Any V.
+//    carry). Any V. Its prefix sums are exact over the whole row: each entry
+//    p > 0 becomes q = rint(p * 2^s) at one power-of-two scale per row with
+//    sum(q) < 2^62, and the id is the smallest j whose integer prefix exceeds
+//    T = min(floor(u * Q), Q - 1); that j always has q >= 1.
 #include "ts_device.h"
 #include "ts_exchange.h"
 #include "ts_launch.h"
@@ -179,39 +173,34 @@ template <int F, bool VEC>
 __global__ __launch_bounds__(CT) void ts_sample_chunks(SampleArgs a) {
     extern __shared__ __align__(16) float dyn[];
     __shared__ float redf[CW];
-    __shared__ uint64_t red64[CW];
-    __shared__ float row_sum;
-    __shared__ uint64_t row_base, row_total;
+    __shared__ ChunkRange row_range;
     constexpr int C = CT * 4 * F;
     const int lane = threadIdx.x;
     int64_t item = blockIdx.x;
     if (item >= a.items) return;
-    // the next item's chunk is loaded while this one waits on its row
+    // the next item's chunk (and the lane's uniform of its row) is loaded while
+    // this one waits on its row
     float p[4 * F], np[4 * F];
-    unsigned long long own_f = 0, own_q = 0, next_f = 0, next_q = 0;
+    unsigned long long own_f = 0, next_f = 0;
+    float u0 = 0.0f, nu0 = 0.0f;
     {
         const int64_t row = item / a.nch, c = item - row * a.nch;
         load_chunk<CT, F, VEC, true>(a.probs + row * a.V, c * C, a.V, p, 0.0f);
-        if (lane == 0) {
-            own_f = slot_load(a.fslots + row * kSlotStride + c);
-            own_q = slot_load(a.qslots + row * kSlotStride + c);
-        }
+        if (lane < a.K) u0 = a.uniforms[row * a.K + lane];
+        if (lane == 0) own_f = slot_load(a.fslots + row * kSlotStride + c);
     }
     for (; item < a.items; item += gridDim.x) {
         const int64_t row = item / a.nch;
         const int64_t c = item - row * a.nch;
         unsigned long long* fs = a.fslots + row * kSlotStride;
-        unsigned long long* qs = a.qslots + row * kSlotStride;
         const int64_t nitem = item + gridDim.x;
         if (nitem < a.items) {
             const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
             load_chunk<CT, F, VEC, true>(a.probs + nr * a.V, nc * C, a.V, np, 0.0f);
-            if (lane == 0) {
-                next_f = slot_load(a.fslots + nr * kSlotStride + nc);
-                next_q = slot_load(a.qslots + nr * kSlotStride + nc);
-            }
+            if (lane < a.K) nu0 = a.uniforms[nr * a.K + lane];
+            if (lane == 0) next_f = slot_load(a.fslots + nr * kSlotStride + nc);
         }
-        // exchange 1: float sum of the positive entries -> the row's scale
+        // the chunk's weight: the float sum of its positive entries
         float fsum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4 * F; ++i) fsum += (p[i] > 0.0f) ? p[i] : 0.0f;
@@ -221,62 +210,33 @@ __global__ __launch_bounds__(CT) void ts_sample_chunks(SampleArgs a) {
             publish(fs, c, a.nch, tf, __float_as_uint(fsum) & 0x7fffffffu);   // a sum of positives
             unsigned long long v[kSlotsPerLane];
             wait_row(fs, a.nch, tf, 0ull, v, a.spin_limit, a.err);
-            float tot = 0.0f;
+            float w[kSlotsPerLane];
 #pragma unroll
-            for (int j = 0; j < kSlotsPerLane; ++j) tot += __uint_as_float(static_cast<uint32_t>(v[j]));
-            tot = wave_reduce<SumOp>(tot);   // same slots, same order in every workgroup of the row
-            if (lane == 0) row_sum = tot;
+            for (int j = 0; j < kSlotsPerLane; ++j) w[j] = __uint_as_float(static_cast<uint32_t>(v[j]));
+            const ChunkRange r = chunk_range(w, c);
+            if (lane == 0) row_range = r;
         }
         __syncthreads();
-        const float total = row_sum;
-        const bool valid = total > 0.0f && total < __builtin_huge_valf();
-        const int s = valid ? scale_exponent(total) : 0;
-        // exchange 2: exact integer sums (published even for an invalid row, to keep the tags)
-        uint64_t qc = 0;
-        if (valid) {
-#pragma unroll
-            for (int i = 0; i < 4 * F; ++i) qc += fixed_point(p[i], s);
-        }
-        qc = block_sum_u64<CW>(qc, red64);
-        if (lane < kWave) {
-            const unsigned long long tq = next_tag(own_q);
-            publish(qs, c, a.nch, tq, qc);
-            unsigned long long v[kSlotsPerLane];
-            wait_row(qs, a.nch, tq, 0ull, v, a.spin_limit, a.err);
-            uint64_t before = 0, tot = 0;
-#pragma unroll
-            for (int j = 0; j < kSlotsPerLane; ++j) {
-                const int64_t i = lane + static_cast<int64_t>(j) * kWave;
-                tot += v[j];
-                before += (i < c) ? v[j] : 0;
-            }
-            before = wave_sum_u64(before);
-            tot = wave_sum_u64(tot);
-            if (lane == 0) {
-                row_base = before;
-                row_total = tot;
-            }
-        }
-        __syncthreads();
-        const uint64_t base = row_base, Q = row_total;
+        const ChunkRange r = row_range;
         const float* urow = a.uniforms + row * a.K;
         int32_t* idrow = a.out_ids + row * a.K;
-        if (!valid || Q == 0) {
+        if (r.total == 0) {   // no positive entry (or a sum that is not finite)
             if (c == 0)
                 for (int64_t kk = lane; kk < a.K; kk += CT) idrow[kk] = -1;
-        } else {
+        } else if (r.width > 0) {
+            // the chunk's own scale: each entry <= fsum < 2^e, chunk total < 2^62
             const float* pr = a.probs + row * a.V;
             const int64_t c0 = c * C;
             const int64_t V = a.V;
             auto fetch = [=](int j, int o, float (&v)[4]) { load_group4<CT>(pr, c0, V, j, o, 0.0f, v); };
-            resolve_chunk<CT, F>(p, reinterpret_cast<unsigned char*>(dyn), s, base, qc, Q, c0, urow, a.K, idrow,
-                                 fetch);
+            resolve_chunk<CT, F>(p, reinterpret_cast<unsigned char*>(dyn), scale_exponent(fsum), r, c0, u0, urow,
+                                 a.K, idrow, fetch);
         }
 #pragma unroll
         for (int i = 0; i < 4 * F; ++i) p[i] = np[i];
         own_f = next_f;
-        own_q = next_q;
-        __syncthreads();   // row broadcasts are rewritten by the next item
+        u0 = nu0;
+        __syncthreads();   // the row range and the resolve table are rewritten by the next item
     }
 }
 

@@ -127,6 +127,12 @@ struct FusedOcc {
     static constexpr int waves_per_eu = MODE == kFusedProbs ? probs_only : (F <= 2 ? 4 : (F == 4 ? 3 : 2));
 };
 
+// Fixed-point scale of a sampling chunk of C columns: its exponentials are
+// <= 1, so with 2^s = 2^61 / C its integer total stays <= 2^61.
+constexpr int ilog2(int v) { return v > 1 ? 1 + ilog2(v / 2) : 0; }
+template <int C>
+constexpr int kChunkScaleExp = 61 - ilog2(C);
+
 // LDS of a sampling mode: see resolve_chunk.
 template <int F>
 constexpr size_t fused_sample_lds() {
@@ -137,9 +143,8 @@ template <int F, bool VEC, int MODE>
 __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fused(SoftmaxArgs a) {
     extern __shared__ __align__(16) float dyn[];
     __shared__ float red[NW];
-    __shared__ uint64_t red64[NW];
     __shared__ float chunk_scale;
-    __shared__ uint64_t row_base, row_total;
+    __shared__ ChunkRange row_range;
     constexpr bool SAMPLE = MODE != kFusedProbs;
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
@@ -147,21 +152,26 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
     if (item >= a.items) return;
 
     float x[4 * F], nx[4 * F];
-    // lane 0: old values of the item's own slots (and of the next item's)
-    unsigned long long own = 0, next_own = 0, own_q = 0, next_own_q = 0;
+    // mask words of the current and the next chunk: applied only when the
+    // chunk's values are used, so the prefetch below never waits on its loads
+    uint32_t mw[2] = {0u, 0u}, nmw[2] = {0u, 0u};
+    // lane 0: old value of the item's own slot (and of the next item's)
+    unsigned long long own = 0, next_own = 0;
+    // sampling: the lane's uniform for target `lane` of the item's row (and the next's)
+    float u0 = 0.0f, nu0 = 0.0f;
     {
         const int64_t row = item / a.nch, c = item - row * a.nch;
-        load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x, kNegInf, mask_row(a, row));
-        if (lane == 0) {
-            own = slot_load(a.slots + row * kSlotStride + c);
-            if (SAMPLE) own_q = slot_load(a.qslots + row * kSlotStride + c);
-        }
+        load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x, kNegInf);
+        if (a.allowed) load_mask_words<NT, F>(mask_row(a, row), c * C, a.V, mw);
+        if (SAMPLE && lane < a.K) u0 = a.uniforms[row * a.K + lane];
+        if (lane == 0) own = slot_load(a.slots + row * kSlotStride + c);
     }
     for (; item < a.items; item += gridDim.x) {
         const int64_t row = item / a.nch;
         const int64_t c = item - row * a.nch;
         const float k = exp2_scale(a.temps[row]);
         unsigned long long* rs = a.slots + row * kSlotStride;
+        if (a.allowed) apply_mask_words<NT, F>(c * C, a.V, mw, x);
 
         // chunk partial: pm = max, pl = sum exp2((x - shift) k); x keeps the exponentials
         float m = kNegInf;
@@ -188,11 +198,10 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
         const int64_t nitem = item + gridDim.x;
         if (nitem < a.items) {
             const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
-            load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx, kNegInf, mask_row(a, nr));
-            if (lane == 0) {
-                next_own = slot_load(a.slots + nr * kSlotStride + nc);
-                if (SAMPLE) next_own_q = slot_load(a.qslots + nr * kSlotStride + nc);
-            }
+            load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx, kNegInf);
+            if (a.allowed) load_mask_words<NT, F>(mask_row(a, nr), nc * C, a.V, nmw);
+            if (SAMPLE && lane < a.K) nu0 = a.uniforms[nr * a.K + lane];
+            if (lane == 0) next_own = slot_load(a.slots + nr * kSlotStride + nc);
         }
 
         // wave 0 waits for the row's partials and combines them: gm = max pm,
@@ -205,77 +214,68 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
 #pragma unroll
             for (int j = 0; j < kSlotsPerLane; ++j) mm = fmaxf(mm, __uint_as_float(static_cast<uint32_t>(v[j])));
             const float gsh = guarded_shift(wave_reduce<MaxOp>(mm));
+            float wgt[kSlotsPerLane];   // the chunks' shares of the row, unnormalised
             float ll = 0.0f;
 #pragma unroll
             for (int j = 0; j < kSlotsPerLane; ++j) {
                 const float vm = __uint_as_float(static_cast<uint32_t>(v[j]));
                 const float vl = __uint_as_float(static_cast<uint32_t>(v[j] >> 32));
-                ll += masked_term(vm, vl * exp2_hw((vm - gsh) * k));
+                wgt[j] = masked_term(vm, vl * exp2_hw((vm - gsh) * k));
+                ll += wgt[j];
             }
             const float gl = wave_reduce<SumOp>(ll);
+            if constexpr (SAMPLE) {
+                const ChunkRange r = chunk_range(wgt, c);
+                if (lane == 0) row_range = r;
+            }
             if (lane == 0) chunk_scale = masked_term(pm, exp2_hw((pm - gsh) * k) * (1.0f / gl));
         }
         __syncthreads();
         const float scale = chunk_scale;
-#pragma unroll
-        for (int i = 0; i < 4 * F; ++i) x[i] *= scale;    // the probabilities
-        if (MODE == kFusedProbs) store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
 
-        if constexpr (SAMPLE) {
-            // second exchange: exact integer sums of the chunks' fixed-point weights
-            uint64_t qc = 0;
+        if constexpr (!SAMPLE) {
 #pragma unroll
-            for (int i = 0; i < 4 * F; ++i) qc += fixed_point(x[i], kProbScaleExp);
-            qc = block_sum_u64<NW>(qc, red64);
-            const unsigned long long tq = next_tag(own_q);
-            unsigned long long* qs = a.qslots + row * kSlotStride;
-            if (lane < kWave) {
-                publish(qs, c, a.nch, tq, qc);
-                unsigned long long v[kSlotsPerLane];
-                wait_row(qs, a.nch, tq, 0ull, v, a.spin_limit, a.err);
-                uint64_t before = 0, total = 0;
-#pragma unroll
-                for (int j = 0; j < kSlotsPerLane; ++j) {
-                    const int64_t i = lane + static_cast<int64_t>(j) * kWave;
-                    total += v[j];
-                    before += (i < c) ? v[j] : 0;
-                }
-                before = wave_sum_u64(before);
-                total = wave_sum_u64(total);
-                if (lane == 0) {
-                    row_base = before;
-                    row_total = total;
-                }
-            }
-            __syncthreads();
-            const uint64_t base = row_base, Q = row_total;
+            for (int i = 0; i < 4 * F; ++i) x[i] *= scale;    // the probabilities
+            store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+        } else {
+            // draw from the chunk's exponentials e = exp2((x - sh) k) <= 1: integer
+            // weights at 2^s with s = 61 - log2(C) keep the chunk total below 2^61
+            const ChunkRange r = row_range;
             const float* urow = a.uniforms + row * a.K;
             int32_t* idrow = a.out_ids + row * a.K;
-            if (Q == 0) {   // no positive probability (a row with no finite logit)
+            if (r.total == 0) {   // no finite logit in the row
                 if (c == 0)
                     for (int64_t kk = lane; kk < a.K; kk += NT) idrow[kk] = -1;
-            } else {
+            } else if (r.width > 0) {   // a chunk of weight 0 holds no target
                 const float* xr = a.logits + row * a.V;
                 const uint32_t* mrow = mask_row(a, row);
                 const int64_t c0 = c * C;
                 const int64_t V = a.V;
-                // p = exp2((x - sh) k) * scale, as computed above for x[]
+                // e = exp2((x - sh) k), as computed above for x[]
                 auto fetch = [=](int j, int o, float (&v)[4]) {
                     load_group4<NT>(xr, c0, V, j, o, kNegInf, v, mrow);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = exp2_hw((v[e] - sh) * k) * scale;
+                    for (int e = 0; e < 4; ++e) v[e] = exp2_hw((v[e] - sh) * k);
                 };
-                resolve_chunk<NT, F>(x, reinterpret_cast<unsigned char*>(dyn), kProbScaleExp, base, qc, Q, c0,
+                resolve_chunk<NT, F>(x, reinterpret_cast<unsigned char*>(dyn), kChunkScaleExp<C>, r, c0, u0,
                                      urow, a.K, idrow, fetch);
             }
-            own_q = next_own_q;
-            // written only now: with probs_out == logits the draw above re-reads logits
-            if (MODE == kFusedProbsIds) store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+            // written only now, and only once every lane's draw is done: with
+            // probs_out == logits the draw above re-reads the chunk's logits
+            if (MODE == kFusedProbsIds) {
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 4 * F; ++i) x[i] *= scale;
+                store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4 * F; ++i) x[i] = nx[i];
+        mw[0] = nmw[0];
+        mw[1] = nmw[1];
         own = next_own;
-        __syncthreads();   // chunk_scale and the row broadcasts are rewritten by the next item
+        u0 = nu0;
+        __syncthreads();   // chunk_scale, the row range and the resolve table are rewritten by the next item
     }
 }
 
@@ -366,13 +366,21 @@ const void* fused_fn() { return reinterpret_cast<const void*>(&ts_fused<F, VEC, 
 template <int F, bool VEC>
 size_t fused_lds(int mode) { return mode == kFusedProbs ? 0 : fused_sample_lds<F>(); }
 
+// The sampling modes are built for chunks of at most 8192 columns (F <= 8).
+constexpr int kMaxSampleF = 8;
+
 template <int F, bool VEC>
 hipError_t fused_impl(const SoftmaxArgs& a, int mode, int64_t grid, hipStream_t s) {
     const dim3 g(static_cast<uint32_t>(grid));
     const size_t lds = fused_lds<F, VEC>(mode);
-    if (mode == kFusedProbs) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbs>), g, dim3(NT), lds, s, a);
-    else if (mode == kFusedProbsIds) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbsIds>), g, dim3(NT), lds, s, a);
-    else hipLaunchKernelGGL((ts_fused<F, VEC, kFusedIds>), g, dim3(NT), lds, s, a);
+    if (mode == kFusedProbs) {
+        hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbs>), g, dim3(NT), lds, s, a);
+    } else if constexpr (F <= kMaxSampleF) {
+        if (mode == kFusedProbsIds) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbsIds>), g, dim3(NT), lds, s, a);
+        else hipLaunchKernelGGL((ts_fused<F, VEC, kFusedIds>), g, dim3(NT), lds, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -383,8 +391,13 @@ hipError_t fused_cap_impl(int mode, int64_t* cap) {
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const void* fn = mode == kFusedProbs ? fused_fn<F, VEC, kFusedProbs>()
-                     : mode == kFusedProbsIds ? fused_fn<F, VEC, kFusedProbsIds>() : fused_fn<F, VEC, kFusedIds>();
+    const void* fn = fused_fn<F, VEC, kFusedProbs>();
+    if (mode != kFusedProbs) {
+        if constexpr (F <= kMaxSampleF)
+            fn = mode == kFusedProbsIds ? fused_fn<F, VEC, kFusedProbsIds>() : fused_fn<F, VEC, kFusedIds>();
+        else
+            return hipErrorInvalidValue;
+    }
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, fused_lds<F, VEC>(mode));
     if (e != hipSuccess) return e;
     *cap = static_cast<int64_t>(per_cu) * cus;

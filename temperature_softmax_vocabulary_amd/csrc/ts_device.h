@@ -119,6 +119,45 @@ __device__ __forceinline__ void apply_allowed(const uint32_t* __restrict__ mrow,
         if (!((bits >> e) & 1u)) v[e] = kNegInf;
 }
 
+// The mask words of a whole chunk, two per lane. Lane t = 64 w + l of the
+// workgroup needs, for group j, word (j NT + t) / 8 = j NT/8 + 8 w + l/8 of the
+// chunk's words: per wave, 8 consecutive words per group. Lane l keeps the
+// words of groups 2 (l / 8) and 2 (l / 8) + 1 at index l % 8, so a group's word
+// is always in the same register of another lane of the same wave, fetched by
+// one cross-lane read (ds_bpermute) when the mask is applied. The loads carry
+// no branch (the index is clamped to the row's last word), so they stay in
+// flight with the data loads until the values are used.
+template <int NT, int F>
+__device__ __forceinline__ void load_mask_words(const uint32_t* __restrict__ mrow, int64_t c0, int64_t V,
+                                                uint32_t (&mw)[2]) {
+    static_assert(F <= 16, "two words per lane cover at most 16 groups");
+    const int l = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int64_t last = (V - 1) >> 5;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = 2 * (l >> 3) + h;
+        const int64_t idx = (c0 >> 5) + static_cast<int64_t>(j) * (NT / 8) + 8 * w + (l & 7);
+        mw[h] = mrow[idx < last ? idx : last];
+    }
+}
+
+// x[4 j + e] = -inf where the id is not allowed (bits past V count as allowed:
+// those columns already hold the fill value).
+template <int NT, int F>
+__device__ __forceinline__ void apply_mask_words(int64_t c0, int64_t V, const uint32_t (&mw)[2],
+                                                 float (&x)[4 * F]) {
+    const int t = threadIdx.x, l = t & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+        const uint32_t word = static_cast<uint32_t>(__shfl(static_cast<int>(mw[j & 1]), (j >> 1) * 8 + (l >> 3), kWave));
+        const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+        const uint32_t bits = (col < V) ? (word >> (col & 31)) : 0xFu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (!((bits >> e) & 1u)) x[4 * j + e] = kNegInf;
+    }
+}
+
 template <int NT, int F, bool VEC, bool NT_LOAD>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t c0, int64_t V,
                                            float (&x)[4 * F], float fill = kNegInf,
@@ -153,17 +192,9 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_
         }
     }
     if (mrow) {
-        uint32_t w[F];
-#pragma unroll
-        for (int j = 0; j < F; ++j) {
-            const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
-            w[j] = (col < V) ? (mrow[col >> 5] >> (col & 31)) : 0xFu;
-        }
-#pragma unroll
-        for (int j = 0; j < F; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (!((w[j] >> e) & 1u)) x[4 * j + e] = kNegInf;
+        uint32_t mw[2];
+        load_mask_words<NT, F>(mrow, c0, V, mw);
+        apply_mask_words<NT, F>(c0, V, mw, x);
     }
 }
 

@@ -13,16 +13,13 @@ constexpr int kChunkThreads = 256;
 constexpr int kMinChunk = 1024;
 constexpr int kMaxChunk = 16384;
 
-// Slots per row for the in-kernel exchanges (ts_exchange.h): the chunked
+// Slots per row for the in-kernel exchange (ts_exchange.h): the chunked
 // kernels run only when a row has at most this many chunks. Each stream's
-// workspace holds three slot sets: softmax partials (pm, pl), sampler float
-// sums, sampler integer sums.
+// workspace holds two slot sets: the fused kernel's chunk partials (pm, pl),
+// and the chunked sampler's float sums.
 constexpr int64_t kSlotStride = 256;
-constexpr int kSlotSets = 3;
-constexpr int kSetPartials = 0, kSetFloatSums = 1, kSetIntSums = 2;
-
-// Fixed-point scale 2^60 for normalised probabilities (each <= 1, sum ~ 1).
-constexpr int kProbScaleExp = 60;
+constexpr int kSlotSets = 2;
+constexpr int kSetPartials = 0, kSetFloatSums = 1;
 
 // Largest row the resident one-workgroup-per-row kernel holds in registers.
 constexpr int kRowwiseThreads = 1024;
@@ -40,7 +37,6 @@ struct SoftmaxArgs {
     int64_t items;         // B * nch
     float2* part;          // [B * nch] chunk partials (pm, pl) of the split kernels
     unsigned long long* slots;   // [B * kSlotStride] tagged (pm, pl) slots of the fused kernel
-    unsigned long long* qslots;  // [B * kSlotStride] tagged integer-sum slots (fused sampling)
     uint32_t* err;         // device error flags (bit 0: a bounded wait ran out)
     uint32_t spin_limit;   // polls before a fused wait gives up
     // fused softmax-and-sample only
@@ -69,7 +65,6 @@ struct SampleArgs {
     int64_t nch;
     int64_t items;
     unsigned long long* fslots;  // [B * kSlotStride] tagged float-sum slots
-    unsigned long long* qslots;  // [B * kSlotStride] tagged integer-sum slots
     uint32_t* err;
     uint32_t spin_limit;
 };

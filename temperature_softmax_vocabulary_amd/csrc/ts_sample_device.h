@@ -8,13 +8,24 @@
 // row's inclusive prefix sums in id order, the id is the smallest j with
 // C[j] > u * C[V-1].
 //
-// Exactness: each entry p > 0 becomes the integer q = rint(p * 2^s), with one
-// power of two 2^s per row, chosen so that the row's integer total Q stays
-// below 2^62. Scaling by a power of two is exact, so q depends only on p and s;
-// integer sums do not depend on the order of addition. With the target
-// T = min(floor(u * Q), Q - 1) the id is the smallest j with Q[j] > T, and
-// Q[j] > T >= Q[j-1] forces q[j] >= 1: an entry that is not > 0 (a masked id)
-// is never drawn, whichever lanes and workgroups add which parts.
+// How the chunked kernels form the prefix sums, with one exchange per row:
+//  * Across chunks. Every chunk publishes one float weight (its share of the
+//    row). Each workgroup of the row turns the row's weights into integers at
+//    one power-of-two scale (chunk_range) and takes exact integer prefix sums:
+//    all of them compute the same integers from the same slot values, so the
+//    chunks' ranges [base, base + width) tile [0, Q) with no gap or overlap,
+//    and the chunk whose range holds the target T = min(floor(u Q), Q - 1)
+//    resolves it. A chunk with no positive entry has width 0 and never does.
+//  * Inside a chunk. Each entry e > 0 becomes q = rint(e * 2^s) at a
+//    power-of-two scale of the chunk, and the integer prefix sums of the q are
+//    exact whatever the order of addition. T is carried into the chunk's units
+//    in double precision and clamped to its integer total L; the id is the
+//    smallest column whose prefix exceeds it. That column always has q >= 1,
+//    so an entry that is not > 0 (a masked id) is never drawn.
+// The draw therefore follows the rule up to the float rounding of the chunk
+// weights (about 1e-7 of the row total). When the weights and entries are
+// dyadic and their float sums exact, every step is exact and the ids are the
+// rule's ids exactly.
 #pragma once
 
 #include "ts_device.h"
@@ -48,106 +59,103 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
     return v;
 }
 
-// Sum over the workgroup (NW waves); lds holds NW values. Returned to all lanes.
-template <int NW>
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* lds) {
-    v = wave_sum_u64(v);
-    if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = v;
-    __syncthreads();
-    uint64_t r = 0;
+// A chunk's share of its row's integer CDF.
+struct ChunkRange {
+    uint64_t base;    // integer prefix of the chunks before it
+    uint64_t width;   // its own integer weight
+    uint64_t total;   // the row's integer total Q (0: nothing can be drawn)
+};
+
+// Called by the 64 lanes of one wave with w[j] = float weight of chunk
+// lane + 64 j (0 for chunks past the row's end or without a positive entry);
+// returns chunk c's range to every lane. The scale comes from the float total
+// (each integer weight < 2^61, so the total < 2^62); reductions run in a fixed
+// order, so every workgroup of the row gets the same integers.
+template <int N>
+__device__ __forceinline__ ChunkRange chunk_range(const float (&w)[N], int64_t c) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float tot = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) r += lds[i];
-    __syncthreads();
+    for (int j = 0; j < N; ++j) tot += w[j];
+    tot = wave_reduce<SumOp>(tot);
+    ChunkRange r = {0, 0, 0};
+    if (!(tot > 0.0f) || !(tot < __builtin_huge_valf())) return r;
+    const int s = scale_exponent(tot);
+    uint64_t before = 0, mine = 0, all = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const int64_t i = lane + static_cast<int64_t>(j) * kWave;
+        const uint64_t q = fixed_point(w[j], s);
+        all += q;
+        before += (i < c) ? q : 0;
+        mine += (i == c) ? q : 0;
+    }
+    r.base = wave_sum_u64(before);
+    r.width = wave_sum_u64(mine);
+    r.total = wave_sum_u64(all);
     return r;
 }
-
-// Exclusive prefix over lanes in threadIdx order; lds holds NW values.
-template <int NW>
-__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* lds) {
-    const int ln = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    uint64_t x = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint64_t y = __shfl_up(x, d, kWave);
-        if (ln >= d) x += y;
-    }
-    if (ln == kWave - 1) lds[wv] = x;
-    __syncthreads();
-    uint64_t before = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) before += (i < wv) ? lds[i] : 0;
-    __syncthreads();
-    return before + x - v;
-}
-
-// Targets per batch held in LDS by resolve_chunk.
-constexpr int kTargetBatch = 256;
 
 // LDS bytes resolve_chunk needs for NT lanes and chunks of F groups.
 template <int NT, int F>
 constexpr size_t resolve_lds_bytes() {
-    return kTargetBatch * sizeof(uint64_t)              // targets of a batch
-           + static_cast<size_t>(F) * NT * sizeof(uint64_t)   // column-order prefix per (group, lane)
+    return static_cast<size_t>(F) * NT * sizeof(uint64_t)          // column-order prefix per (group, lane)
            + static_cast<size_t>(NT / kWave) * F * sizeof(uint64_t);   // wave totals per group
 }
 
-// Resolve, inside one chunk, every target of the row that falls in it.
+// Resolve every target of the row that falls in chunk range r.
 //
-// The chunk's entries p (the probabilities) sit in registers in the layout of
-// load_chunk: F groups of NT * 4 consecutive columns, lane t holding columns
-// (j NT + t) 4 + e of group j, so (group, lane) order is column order. The
-// lanes' per-group integer sums are scanned across the workgroup into an LDS
-// table pre[j NT + t] of column-order exclusive prefixes (all groups in one
-// pass: wave shuffles, then one LDS round for the wave totals). The row's
-// uniforms become integer targets a batch at a time (one per lane, loads in
-// parallel) in LDS. Each lane then takes its own share of the batch's targets
-// that fall in [base, base + Qc): the owner of chunk-relative target Tc is the
-// largest m with pre[m] <= Tc (binary search; an entry whose sum is 0 has the
-// same prefix as the next one, so the largest is never empty), and
-// fetch(j, t, v) reloads the owner's 4 entries -- bitwise the values summed
-// here -- for a walk to the smallest column whose running sum exceeds Tc.
-// `lds` points at resolve_lds_bytes<NT, F>() bytes; all lanes must call.
+// e[] holds the chunk's entries in the layout of load_chunk: F groups of
+// NT * 4 consecutive columns, lane t holding columns (j NT + t) 4 + e of group
+// j, so (group, lane) order is column order. Lane t takes targets t, t + NT,
+// ... of the row; u0 is its uniform for target t (loaded ahead by the caller).
+// Only when some target lands in the chunk are the lanes' per-group integer
+// sums at scale 2^s scanned into an LDS table pre[j NT + t] of column-order
+// exclusive prefixes (all groups in one pass: wave shuffles, then one LDS round
+// for the wave totals). The owner of chunk-relative target Tc is the largest m
+// with pre[m] <= Tc (binary search; an entry whose sum is 0 has the same prefix
+// as the next one, so the largest is never empty), and fetch(j, t, v) reloads
+// the owner's 4 entries -- bitwise the values summed here -- for a walk to the
+// smallest column whose running sum exceeds Tc. `lds` points at
+// resolve_lds_bytes<NT, F>() bytes; all lanes must call; r.width > 0 implies
+// that the chunk holds an entry e with rint(e 2^s) >= 1.
 template <int NT, int F, class Fetch>
-__device__ __forceinline__ void resolve_chunk(const float (&p)[4 * F], unsigned char* lds, int s,
-                                              uint64_t base, uint64_t Qc, uint64_t Q, int64_t c0,
-                                              const float* __restrict__ urow, int64_t K,
+__device__ __forceinline__ void resolve_chunk(const float (&e)[4 * F], unsigned char* lds, int s, ChunkRange r,
+                                              int64_t c0, float u0, const float* __restrict__ urow, int64_t K,
                                               int32_t* __restrict__ idrow, const Fetch& fetch) {
     constexpr int NW = NT / kWave;
-    uint64_t* tgt = reinterpret_cast<uint64_t*>(lds);
-    uint64_t* pre = tgt + kTargetBatch;
+    uint64_t* pre = reinterpret_cast<uint64_t*>(lds);
     uint64_t* wt = pre + F * NT;
     const int t = threadIdx.x;
     const int ln = t & (kWave - 1), wv = t / kWave;
     bool scanned = false;
-    for (int64_t kb = 0; kb < K; kb += kTargetBatch) {
-        const int n = static_cast<int>(K - kb < kTargetBatch ? K - kb : kTargetBatch);
-        int hit = 0;
-        for (int i = t; i < n; i += NT) {
-            const uint64_t T = target_of(urow[kb + i], Q);
-            tgt[i] = T;
-            hit |= (T >= base && T - base < Qc) ? 1 : 0;
+    uint64_t L = 0;   // the chunk's integer total
+    for (int64_t kb = 0; kb < K; kb += NT) {
+        const int64_t k = kb + t;
+        uint64_t T = 0;
+        bool own = false;
+        if (k < K) {
+            T = target_of(kb == 0 ? u0 : urow[k], r.total);
+            own = T >= r.base && T - r.base < r.width;
         }
-        if (!__syncthreads_or(hit)) continue;      // also orders the tgt writes
+        if (!__syncthreads_or(own)) continue;
         if (!scanned) {
-            // all groups at once: wave scans, one LDS round for the wave totals
-            uint64_t sg[F], x[F];
+            // one group at a time (few live registers): wave-inclusive scans of
+            // the lanes' 4-entry sums, kept in pre[] as wave-exclusive prefixes,
+            // and the wave totals in wt[]; then one LDS round adds the offsets
 #pragma unroll
             for (int j = 0; j < F; ++j) {
-                sg[j] = fixed_point(p[4 * j], s) + fixed_point(p[4 * j + 1], s) + fixed_point(p[4 * j + 2], s) +
-                        fixed_point(p[4 * j + 3], s);
-                x[j] = sg[j];
-            }
+                const uint64_t sg = fixed_point(e[4 * j], s) + fixed_point(e[4 * j + 1], s) +
+                                    fixed_point(e[4 * j + 2], s) + fixed_point(e[4 * j + 3], s);
+                uint64_t x = sg;
 #pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-#pragma unroll
-                for (int j = 0; j < F; ++j) {
-                    const uint64_t y = __shfl_up(x[j], d, kWave);
-                    if (ln >= d) x[j] += y;
+                for (int d = 1; d < kWave; d <<= 1) {
+                    const uint64_t y = __shfl_up(x, d, kWave);
+                    if (ln >= d) x += y;
                 }
+                pre[j * NT + t] = x - sg;
+                if (ln == kWave - 1) wt[wv * F + j] = x;
             }
-            if (ln == kWave - 1)
-#pragma unroll
-                for (int j = 0; j < F; ++j) wt[wv * F + j] = x[j];
             __syncthreads();
             uint64_t run = 0;
 #pragma unroll
@@ -159,33 +167,33 @@ __device__ __forceinline__ void resolve_chunk(const float (&p)[4 * F], unsigned 
                     total += v;
                     before += (w < wv) ? v : 0;
                 }
-                pre[j * NT + t] = run + before + x[j] - sg[j];
+                pre[j * NT + t] += run + before;
                 run += total;
             }
+            L = run;
             __syncthreads();   // pre complete before any lane searches it
             scanned = true;
         }
-        for (int i = t; i < n; i += NT) {
-            const uint64_t T = tgt[i];
-            if (T < base || T - base >= Qc) continue;
-            const uint64_t Tc = T - base;
-            int lo = 0, hi = F * NT - 1;             // largest m with pre[m] <= Tc (pre[0] = 0)
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (pre[mid] <= Tc) lo = mid; else hi = mid - 1;
-            }
-            const int j = lo / NT, o = lo - j * NT;
-            float v[4];
-            fetch(j, o, v);
-            uint64_t acc = pre[lo];
-            int e = 0;
-            for (; e < 3; ++e) {
-                acc += fixed_point(v[e], s);
-                if (acc > Tc) break;
-            }
-            idrow[kb + i] = static_cast<int32_t>(c0 + (static_cast<int64_t>(j) * NT + o) * 4 + e);
+        if (!own) continue;
+        // the target's place inside the chunk, in the chunk's own units
+        const double f = static_cast<double>(T - r.base) * (static_cast<double>(L) / static_cast<double>(r.width));
+        uint64_t Tc = f < static_cast<double>(L) ? static_cast<uint64_t>(f) : L - 1;
+        if (Tc > L - 1) Tc = L - 1;
+        int lo = 0, hi = F * NT - 1;             // largest m with pre[m] <= Tc (pre[0] = 0)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= Tc) lo = mid; else hi = mid - 1;
         }
-        __syncthreads();   // tgt is rewritten by the next batch
+        const int j = lo / NT, o = lo - j * NT;
+        float v[4];
+        fetch(j, o, v);
+        uint64_t acc = pre[lo];
+        int ee = 0;
+        for (; ee < 3; ++ee) {
+            acc += fixed_point(v[ee], s);
+            if (acc > Tc) break;
+        }
+        idrow[k] = static_cast<int32_t>(c0 + (static_cast<int64_t>(j) * NT + o) * 4 + ee);
     }
 }
 

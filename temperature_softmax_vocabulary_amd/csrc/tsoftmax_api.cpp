@@ -270,7 +270,6 @@ ts_status run_softmax(const float* logits, const float* temps, const uint32_t* a
     const WsView v = ws_view(*w);
     a.part = v.part;
     a.slots = v.sets[tsk::kSetPartials];
-    a.qslots = v.sets[tsk::kSetIntSums];
     a.err = v.err;
     if (plan.variant == TS_VARIANT_FUSED)
         return hip_status(tsk::launch_fused(a, plan.F, vec, tsk::kFusedProbs, grid, stream));
@@ -346,7 +345,6 @@ TS_API ts_status ts_sample(const float* probs, const float* uniforms, int64_t B,
     if (st != TS_OK) return st;
     const WsView v = ws_view(*w);
     a.fslots = v.sets[tsk::kSetFloatSums];
-    a.qslots = v.sets[tsk::kSetIntSums];
     a.err = v.err;
     return hip_status(tsk::launch_sample_chunks(a, F, vec, fused_grid(a.items, a.nch, cap), stream));
 }
@@ -400,7 +398,6 @@ TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, cons
     if (st != TS_OK) return st;
     const WsView v = ws_view(*w);
     a.slots = v.sets[tsk::kSetPartials];
-    a.qslots = v.sets[tsk::kSetIntSums];
     a.err = v.err;
     return hip_status(tsk::launch_fused(a, F, vec, mode, fused_grid(a.items, a.nch, cap), stream));
 }
