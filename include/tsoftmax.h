@@ -143,13 +143,13 @@ ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
  * out_ids  : [B, K] int32. For each (b, k): with C the row's inclusive
  *            prefix sums and target = u * C[V-1], the smallest id j with
  *            C[j] > target; for u = 1 the last id with a positive entry.
- *            Prefix sums are integers: inside a column chunk, the entries in
- *            64-bit fixed point at a power-of-two scale (exact); across chunks,
- *            the chunks' float sums at one power-of-two scale per row, so a
- *            chunk boundary can sit about 1e-7 of the row total away from the
- *            exact one (rows of more than 2,097,152 ids: one exact sum over
- *            the row). The id is always one with a positive entry. A row with
- *            no positive entry (or a sum that is not finite) gives -1.
+ *            Prefix sums are integers: inside each group of 1024 ids, the
+ *            entries in 64-bit fixed point at a power-of-two scale (exact);
+ *            across groups, the groups' float sums at one power-of-two scale
+ *            per row, so a group boundary can sit about 1e-7 of the row total
+ *            away from the exact one. The id is always one with a positive
+ *            entry. A row with no positive entry (or a sum that is not
+ *            finite) gives -1.
  * Errors   : TS_ERR_INVALID_ARGUMENT for B < 0, K < 0, V < 1,
  *            V > INT32_MAX, a NULL pointer when B*K > 0, or out_ids overlapping
  *            probs or uniforms. B == 0 or K == 0 is a no-op.
@@ -158,11 +158,12 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
                     int32_t* out_ids, hipStream_t stream);
 
 /*
- * The softmax and the token draw in one pass over the logits: ts_softmax
- * followed by ts_sample, without writing and re-reading the probabilities
- * unless asked to. The draw consumes the softmax as in the scope paragraph of
- * the pull-request page; every id drawn has a finite logit (results table,
- * sampling row).
+ * The softmax and the token draw in one call: ts_softmax followed by
+ * ts_sample. Without probs_out the probabilities are never written: the logits
+ * are read once for per-group partials, and only the groups that hold a
+ * target are read again. The draw consumes the softmax as in the scope
+ * paragraph of the pull-request page; every id drawn has a finite logit
+ * (results table, sampling row).
  *
  * logits, temps : as for ts_softmax.
  * allowed       : NULL, or an allowed-id bitmask as for ts_softmax_masked.
@@ -170,14 +171,14 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  * probs_out     : [B, V] float32 or NULL. If not NULL it receives the same
  *                 probabilities ts_softmax computes (probs_out == logits is
  *                 allowed); if NULL the probabilities are never written.
- * out_ids       : [B, K] int32. The inverse-CDF rule of ts_sample, applied to
- *                 the probabilities with the same chunked integer prefix sums;
- *                 every id drawn has a finite logit (and an allowed bit); -1
- *                 for a row with none.
- * Limits        : V <= 2,097,152 (256 chunks of 8192 columns per row).
- * Errors        : as ts_softmax and ts_sample; TS_ERR_INVALID_ARGUMENT also for
- *                 V above the limit. K == 0 reduces to ts_softmax (or a no-op
- *                 when probs_out is NULL).
+ * out_ids       : [B, K] int32. The inverse-CDF rule of ts_sample with the
+ *                 same integer prefix sums over groups of 1024 ids; every id
+ *                 drawn has a finite logit (and an allowed bit); -1 for a row
+ *                 with none. With probs_out the draw reads the written
+ *                 probabilities (the ids equal ts_sample's on them); without,
+ *                 it works from the logits (one read of them in all).
+ * Errors        : as ts_softmax and ts_sample. K == 0 reduces to ts_softmax
+ *                 (or a no-op when probs_out is NULL).
  */
 ts_status ts_softmax_sample(const float* logits, const float* temps, const uint32_t* allowed,
                             const float* uniforms, int64_t B, int64_t V, int64_t K, float* probs_out,

@@ -26,7 +26,7 @@ LIB_NOGUARD = os.path.join(HERE, "libtsoftmax_noguard.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
-SOURCES = ["softmax_kernels.hip", "sample_kernel.hip", "measure_kernels.hip", "tsoftmax_api.cpp"]
+SOURCES = ["softmax_kernels.hip", "draw_kernels.hip", "measure_kernels.hip", "tsoftmax_api.cpp"]
 
 # -ffast-math and friends are never used: -inf and NaN semantics are the point.
 COMMON = [

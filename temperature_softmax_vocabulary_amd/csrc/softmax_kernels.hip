@@ -15,14 +15,13 @@
 //            ts_split_finalize_write combines a row's partials and writes the
 //            chunk's probs (finalize fused into the write; logits read twice).
 //  fused   : one kernel; each workgroup keeps its chunk's exponentials in
-//            registers, publishes (pm, pl), waits for the row's other chunks
-//            on a per-row arrival counter, then writes (logits read once).
+//            registers, publishes (pm, pl) in the row's tagged slots, waits
+//            for the row's other chunks, then writes (logits read once).
 //  rowwise : one workgroup per row; the row sits in registers when it fits
 //            (read once), else an online (m, l) sweep and a write sweep.
 #include "ts_device.h"
 #include "ts_exchange.h"
 #include "ts_launch.h"
-#include "ts_sample_device.h"
 
 namespace tsk {
 
@@ -114,38 +113,23 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 // either costs microseconds per workgroup on a multi-XCD part). The host
 // launches no more workgroups than the device holds at once and at least nch.
 //
-// MODE kFusedProbs writes the probabilities. kFusedProbsIds and kFusedIds also
-// draw token ids by inverse CDF (ts_sample_device.h) from the probabilities
-// the chunk holds in registers, through a second exchange of the chunks'
-// exact integer sums; kFusedIds skips writing the probabilities.
+// MODE kFusedProbs writes the probabilities; kFusedProbsSums also writes, per
+// group of kDrawGroup columns (group j of a chunk = lane float4s j NT + t),
+// the sum of its probabilities, for a token draw that follows
+// (draw_kernels.hip).
 // ---------------------------------------------------------------------------
-template <int F, int MODE>
+template <int F>
 struct FusedOcc {
-    // registers hold the current and the next chunk (8 F floats per lane);
-    // the sampling modes need about 60 more for the second exchange
-    static constexpr int probs_only = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
-    static constexpr int waves_per_eu = MODE == kFusedProbs ? probs_only : (F <= 2 ? 4 : (F == 4 ? 3 : 2));
+    // registers hold the current and the next chunk (8 F floats per lane)
+    static constexpr int waves_per_eu = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
 };
 
-// Fixed-point scale of a sampling chunk of C columns: its exponentials are
-// <= 1, so with 2^s = 2^61 / C its integer total stays <= 2^61.
-constexpr int ilog2(int v) { return v > 1 ? 1 + ilog2(v / 2) : 0; }
-template <int C>
-constexpr int kChunkScaleExp = 61 - ilog2(C);
-
-// LDS of a sampling mode: see resolve_chunk.
-template <int F>
-constexpr size_t fused_sample_lds() {
-    return resolve_lds_bytes<NT, F>();
-}
-
 template <int F, bool VEC, int MODE>
-__global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fused(SoftmaxArgs a) {
-    extern __shared__ __align__(16) float dyn[];
+__global__ __launch_bounds__(NT, (FusedOcc<F>::waves_per_eu)) void ts_fused(SoftmaxArgs a) {
+    static_assert(NT * 4 == kDrawGroup, "a chunk group is one draw group");
     __shared__ float red[NW];
+    __shared__ float gsum[MODE == kFusedProbsSums ? F : 1][NW];
     __shared__ float chunk_scale;
-    __shared__ ChunkRange row_range;
-    constexpr bool SAMPLE = MODE != kFusedProbs;
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
     int64_t item = blockIdx.x;
@@ -157,13 +141,10 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
     uint32_t mw[2] = {0u, 0u}, nmw[2] = {0u, 0u};
     // lane 0: old value of the item's own slot (and of the next item's)
     unsigned long long own = 0, next_own = 0;
-    // sampling: the lane's uniform for target `lane` of the item's row (and the next's)
-    float u0 = 0.0f, nu0 = 0.0f;
     {
         const int64_t row = item / a.nch, c = item - row * a.nch;
         load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x, kNegInf);
         if (a.allowed) load_mask_words<NT, F>(mask_row(a, row), c * C, a.V, mw);
-        if (SAMPLE && lane < a.K) u0 = a.uniforms[row * a.K + lane];
         if (lane == 0) own = slot_load(a.slots + row * kSlotStride + c);
     }
     for (; item < a.items; item += gridDim.x) {
@@ -200,7 +181,6 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
             const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
             load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx, kNegInf);
             if (a.allowed) load_mask_words<NT, F>(mask_row(a, nr), nc * C, a.V, nmw);
-            if (SAMPLE && lane < a.K) nu0 = a.uniforms[nr * a.K + lane];
             if (lane == 0) next_own = slot_load(a.slots + nr * kSlotStride + nc);
         }
 
@@ -214,59 +194,34 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
 #pragma unroll
             for (int j = 0; j < kSlotsPerLane; ++j) mm = fmaxf(mm, __uint_as_float(static_cast<uint32_t>(v[j])));
             const float gsh = guarded_shift(wave_reduce<MaxOp>(mm));
-            float wgt[kSlotsPerLane];   // the chunks' shares of the row, unnormalised
             float ll = 0.0f;
 #pragma unroll
             for (int j = 0; j < kSlotsPerLane; ++j) {
                 const float vm = __uint_as_float(static_cast<uint32_t>(v[j]));
                 const float vl = __uint_as_float(static_cast<uint32_t>(v[j] >> 32));
-                wgt[j] = masked_term(vm, vl * exp2_hw((vm - gsh) * k));
-                ll += wgt[j];
+                ll += masked_term(vm, vl * exp2_hw((vm - gsh) * k));
             }
             const float gl = wave_reduce<SumOp>(ll);
-            if constexpr (SAMPLE) {
-                const ChunkRange r = chunk_range(wgt, c);
-                if (lane == 0) row_range = r;
-            }
             if (lane == 0) chunk_scale = masked_term(pm, exp2_hw((pm - gsh) * k) * (1.0f / gl));
         }
         __syncthreads();
         const float scale = chunk_scale;
-
-        if constexpr (!SAMPLE) {
 #pragma unroll
-            for (int i = 0; i < 4 * F; ++i) x[i] *= scale;    // the probabilities
-            store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
-        } else {
-            // draw from the chunk's exponentials e = exp2((x - sh) k) <= 1: integer
-            // weights at 2^s with s = 61 - log2(C) keep the chunk total below 2^61
-            const ChunkRange r = row_range;
-            const float* urow = a.uniforms + row * a.K;
-            int32_t* idrow = a.out_ids + row * a.K;
-            if (r.total == 0) {   // no finite logit in the row
-                if (c == 0)
-                    for (int64_t kk = lane; kk < a.K; kk += NT) idrow[kk] = -1;
-            } else if (r.width > 0) {   // a chunk of weight 0 holds no target
-                const float* xr = a.logits + row * a.V;
-                const uint32_t* mrow = mask_row(a, row);
-                const int64_t c0 = c * C;
-                const int64_t V = a.V;
-                // e = exp2((x - sh) k), as computed above for x[]
-                auto fetch = [=](int j, int o, float (&v)[4]) {
-                    load_group4<NT>(xr, c0, V, j, o, kNegInf, v, mrow);
+        for (int i = 0; i < 4 * F; ++i) x[i] *= scale;    // the probabilities
+        store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+        if constexpr (MODE == kFusedProbsSums) {
+            const int ln = lane & (kWave - 1), wv = lane / kWave;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = exp2_hw((v[e] - sh) * k);
-                };
-                resolve_chunk<NT, F>(x, reinterpret_cast<unsigned char*>(dyn), kChunkScaleExp<C>, r, c0, u0,
-                                     urow, a.K, idrow, fetch);
+            for (int j = 0; j < F; ++j) {
+                const float ws = wave_reduce<SumOp>((x[4 * j] + x[4 * j + 1]) + (x[4 * j + 2] + x[4 * j + 3]));
+                if (ln == 0) gsum[j][wv] = ws;
             }
-            // written only now, and only once every lane's draw is done: with
-            // probs_out == logits the draw above re-reads the chunk's logits
-            if (MODE == kFusedProbsIds) {
-                __syncthreads();
+            __syncthreads();
+            if (lane < F && c * F + lane < a.nsub) {
+                float gs = gsum[lane][0];
 #pragma unroll
-                for (int i = 0; i < 4 * F; ++i) x[i] *= scale;
-                store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
+                for (int w = 1; w < NW; ++w) gs += gsum[lane][w];
+                a.part[row * a.nsub + c * F + lane] = make_float2(gs, 0.0f);
             }
         }
 #pragma unroll
@@ -274,8 +229,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
         mw[0] = nmw[0];
         mw[1] = nmw[1];
         own = next_own;
-        u0 = nu0;
-        __syncthreads();   // chunk_scale, the row range and the resolve table are rewritten by the next item
+        __syncthreads();   // chunk_scale and the group sums are rewritten by the next item
     }
 }
 
@@ -360,27 +314,11 @@ hipError_t split_impl(const SoftmaxArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int F, bool VEC, int MODE>
-const void* fused_fn() { return reinterpret_cast<const void*>(&ts_fused<F, VEC, MODE>); }
-
-template <int F, bool VEC>
-size_t fused_lds(int mode) { return mode == kFusedProbs ? 0 : fused_sample_lds<F>(); }
-
-// The sampling modes are built for chunks of at most 8192 columns (F <= 8).
-constexpr int kMaxSampleF = 8;
-
 template <int F, bool VEC>
 hipError_t fused_impl(const SoftmaxArgs& a, int mode, int64_t grid, hipStream_t s) {
     const dim3 g(static_cast<uint32_t>(grid));
-    const size_t lds = fused_lds<F, VEC>(mode);
-    if (mode == kFusedProbs) {
-        hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbs>), g, dim3(NT), lds, s, a);
-    } else if constexpr (F <= kMaxSampleF) {
-        if (mode == kFusedProbsIds) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbsIds>), g, dim3(NT), lds, s, a);
-        else hipLaunchKernelGGL((ts_fused<F, VEC, kFusedIds>), g, dim3(NT), lds, s, a);
-    } else {
-        return hipErrorInvalidValue;
-    }
+    if (mode == kFusedProbs) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbs>), g, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbsSums>), g, dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -391,14 +329,9 @@ hipError_t fused_cap_impl(int mode, int64_t* cap) {
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const void* fn = fused_fn<F, VEC, kFusedProbs>();
-    if (mode != kFusedProbs) {
-        if constexpr (F <= kMaxSampleF)
-            fn = mode == kFusedProbsIds ? fused_fn<F, VEC, kFusedProbsIds>() : fused_fn<F, VEC, kFusedIds>();
-        else
-            return hipErrorInvalidValue;
-    }
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, fused_lds<F, VEC>(mode));
+    const void* fn = mode == kFusedProbs ? reinterpret_cast<const void*>(&ts_fused<F, VEC, kFusedProbs>)
+                                         : reinterpret_cast<const void*>(&ts_fused<F, VEC, kFusedProbsSums>);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0);
     if (e != hipSuccess) return e;
     *cap = static_cast<int64_t>(per_cu) * cus;
     return hipSuccess;

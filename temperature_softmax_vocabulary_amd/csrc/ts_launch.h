@@ -13,13 +13,16 @@ constexpr int kChunkThreads = 256;
 constexpr int kMinChunk = 1024;
 constexpr int kMaxChunk = 16384;
 
-// Slots per row for the in-kernel exchange (ts_exchange.h): the chunked
-// kernels run only when a row has at most this many chunks. Each stream's
-// workspace holds two slot sets: the fused kernel's chunk partials (pm, pl),
-// and the chunked sampler's float sums.
+// Slots per row for the in-kernel exchange (ts_exchange.h): the fused kernel
+// runs only when a row has at most this many chunks. Each stream's workspace
+// holds one slot set (the fused kernel's chunk partials (pm, pl)).
 constexpr int64_t kSlotStride = 256;
-constexpr int kSlotSets = 2;
-constexpr int kSetPartials = 0, kSetFloatSums = 1;
+constexpr int kSlotSets = 1;
+constexpr int kSetPartials = 0;
+
+// Token draws work on groups of kDrawGroup columns (one float4 per lane of a
+// 256-lane workgroup): per-group partials, then one wave per target.
+constexpr int kDrawGroup = 1024;
 
 // Largest row the resident one-workgroup-per-row kernel holds in registers.
 constexpr int kRowwiseThreads = 1024;
@@ -35,18 +38,17 @@ struct SoftmaxArgs {
     int64_t V;
     int64_t nch;           // chunks per row (split, fused)
     int64_t items;         // B * nch
-    float2* part;          // [B * nch] chunk partials (pm, pl) of the split kernels
+    float2* part;          // split: [B * nch] chunk partials (pm, pl);
+                           // fused with group sums: [B * nsub] (sum of probs, 0) per group
+    int64_t nsub;          // groups of kDrawGroup columns per row (fused with group sums)
     unsigned long long* slots;   // [B * kSlotStride] tagged (pm, pl) slots of the fused kernel
     uint32_t* err;         // device error flags (bit 0: a bounded wait ran out)
     uint32_t spin_limit;   // polls before a fused wait gives up
-    // fused softmax-and-sample only
-    const float* uniforms; // [B, K]
-    int32_t* out_ids;      // [B, K]
-    int64_t K;
 };
 
-// Fused kernel modes: probabilities only; probabilities and ids; ids only.
-constexpr int kFusedProbs = 0, kFusedProbsIds = 1, kFusedIds = 2;
+// Fused kernel modes: probabilities only; probabilities and the per-group sums
+// of the probabilities (for a token draw that follows).
+constexpr int kFusedProbs = 0, kFusedProbsSums = 1;
 
 hipError_t launch_split(const SoftmaxArgs& a, int F, bool vec, hipStream_t s);
 hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int mode, int64_t grid, hipStream_t s);
@@ -54,25 +56,27 @@ hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int mode, int64_t
 hipError_t fused_resident_capacity(int F, bool vec, int mode, int64_t* cap);
 hipError_t launch_rowwise(const SoftmaxArgs& a, bool vec, hipStream_t s);
 
-struct SampleArgs {
-    const float* probs;      // [B, V]
-    const float* uniforms;   // [B, K]
-    int32_t* out_ids;        // [B, K]
+// Token draws (draw_kernels.hip).
+constexpr int kDrawLogits = 0, kDrawProbs = 1;
+struct DrawArgs {
+    const float* x;           // [B, V] logits (kDrawLogits) or probabilities (kDrawProbs)
+    const float* temps;       // [B] (kDrawLogits)
+    const uint32_t* allowed;  // [B, mwords] allowed-id bitmask or null (kDrawLogits)
+    int64_t mwords;
+    const float* uniforms;    // [B, K]
+    int32_t* out_ids;         // [B, K]
+    float2* part;             // [B, nsub] group partials: (max, sum exp2) or (positive sum, 0)
     int64_t B;
     int64_t V;
     int64_t K;
-    // chunked kernel only
-    int64_t nch;
-    int64_t items;
-    unsigned long long* fslots;  // [B * kSlotStride] tagged float-sum slots
-    uint32_t* err;
-    uint32_t spin_limit;
+    int64_t nsub;             // ceil(V / kDrawGroup)
+    int64_t nch;              // workgroups per row of the partials kernel: ceil(V / (kDrawGroup F))
 };
-// One workgroup per row, three sweeps (any V).
-hipError_t launch_sample_rows(const SampleArgs& a, bool vec, hipStream_t s);
-// Chunked, one read: (row, chunk) items over a persistent grid (nch <= kSlotStride).
-hipError_t launch_sample_chunks(const SampleArgs& a, int F, bool vec, int64_t grid, hipStream_t s);
-hipError_t sample_resident_capacity(int F, bool vec, int64_t* cap);
+// Per-group partials over the whole of x (one read), F groups per workgroup.
+hipError_t launch_group_partials(const DrawArgs& a, int F, bool vec, int kind, hipStream_t s);
+// One wave per (row, target): integer CDF over the row's groups, then the
+// group that holds the target resolves it exactly.
+hipError_t launch_draw_resolve(const DrawArgs& a, bool vec, int kind, hipStream_t s);
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, bool vec, hipStream_t s);
 

@@ -141,7 +141,7 @@ struct Plan {
 };
 
 // Workgroups one device holds at once, per kernel (cached per device):
-// kind 0..2 = fused kernel in that mode, kind 3 = chunked sampler.
+// kind = the fused kernel's mode.
 ts_status resident_cap(int kind, int F, bool vec, int64_t* cap) {
     static std::mutex mu;
     static std::map<std::tuple<int, int, int, bool>, int64_t> cache;
@@ -152,8 +152,7 @@ ts_status resident_cap(int kind, int F, bool vec, int64_t* cap) {
     auto it = cache.find(key);
     if (it == cache.end()) {
         int64_t c = 0;
-        const hipError_t e = kind == 3 ? tsk::sample_resident_capacity(F, vec, &c)
-                                       : tsk::fused_resident_capacity(F, vec, kind, &c);
+        const hipError_t e = tsk::fused_resident_capacity(F, vec, kind, &c);
         if (e != hipSuccess) return TS_ERR_HIP;
         it = cache.emplace(key, c).first;
     }
@@ -201,10 +200,19 @@ int64_t fused_grid(int64_t items, int64_t nch, int64_t cap) {
 
 int64_t mask_words(int64_t V) { return (V + 31) / 32; }
 
-ts_status run_softmax(const float* logits, const float* temps, const uint32_t* allowed, int64_t B, int64_t V,
-                      float* out, int variant, int chunk, hipStream_t stream) {
-    if (!sizes_ok(B, V)) return TS_ERR_INVALID_ARGUMENT;
-    if (B == 0) return TS_OK;
+// A softmax call, checked and planned, ready to launch on a workspace.
+struct SoftmaxCall {
+    tsk::SoftmaxArgs a{};
+    Plan plan{};
+    bool vec = false;
+    int64_t grid = 0;
+    int64_t need_b = 0;   // workspace rows (fused slots)
+    int64_t need_p = 0;   // workspace partials (split)
+};
+
+// Argument checks and the work split; launches nothing. B > 0.
+ts_status prepare_softmax(const float* logits, const float* temps, const uint32_t* allowed, int64_t B, int64_t V,
+                          float* out, int variant, int chunk, SoftmaxCall* call) {
     if (!logits || !temps || !out) return TS_ERR_INVALID_ARGUMENT;
     const int64_t xbytes = B * V * 4;
     if (out != logits && overlaps(out, xbytes, logits, xbytes)) return TS_ERR_INVALID_ARGUMENT;
@@ -233,7 +241,8 @@ ts_status run_softmax(const float* logits, const float* temps, const uint32_t* a
         }
     }
 
-    tsk::SoftmaxArgs a{};
+    tsk::SoftmaxArgs& a = call->a;
+    a = tsk::SoftmaxArgs{};
     a.logits = logits;
     a.temps = temps;
     a.allowed = allowed;
@@ -242,48 +251,107 @@ ts_status run_softmax(const float* logits, const float* temps, const uint32_t* a
     a.B = B;
     a.V = V;
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    call->plan = plan;
+    call->vec = vec;
 
     if (plan.variant == TS_VARIANT_ROWWISE) {
         if (B > INT32_MAX) return TS_ERR_INVALID_ARGUMENT;
-        return hip_status(tsk::launch_rowwise(a, vec, stream));
+        return TS_OK;
     }
-
     a.nch = cdiv(V, 1024 * plan.F);
     a.items = B * a.nch;
-    int64_t grid = a.items;
+    call->grid = a.items;
     if (plan.variant == TS_VARIANT_FUSED) {
         int64_t cap = 0;
         ts_status st = resident_cap(tsk::kFusedProbs, plan.F, vec, &cap);
         if (st != TS_OK) return st;
         // The lowest unfinished row must fit the device at once (ts_exchange.h).
         if (a.nch > tsk::kSlotStride || a.nch > cap) return TS_ERR_INVALID_ARGUMENT;
-        grid = fused_grid(a.items, a.nch, cap);
-    } else if (a.items > INT32_MAX) {
-        return TS_ERR_INVALID_ARGUMENT;
+        call->grid = fused_grid(a.items, a.nch, cap);
+        call->need_b = B;
+    } else {
+        if (a.items > INT32_MAX) return TS_ERR_INVALID_ARGUMENT;
+        call->need_p = a.items;
     }
+    return TS_OK;
+}
 
-    std::lock_guard<std::mutex> lk(g_mu);
-    Workspace* w = nullptr;
-    const bool fused = plan.variant == TS_VARIANT_FUSED;
-    ts_status st = ws_get(stream, fused ? B : 0, fused ? 0 : a.items, &w);
-    if (st != TS_OK) return st;
-    const WsView v = ws_view(*w);
+// Called with g_mu held and a workspace sized for the call. With group_sums
+// and the fused split, the kernel also writes the per-group sums of the
+// probabilities to the workspace partials (*sums = true).
+ts_status launch_softmax(SoftmaxCall& call, const WsView& v, bool group_sums, bool* sums, hipStream_t stream) {
+    tsk::SoftmaxArgs& a = call.a;
+    if (sums) *sums = false;
+    if (call.plan.variant == TS_VARIANT_ROWWISE) return hip_status(tsk::launch_rowwise(a, call.vec, stream));
     a.part = v.part;
     a.slots = v.sets[tsk::kSetPartials];
     a.err = v.err;
-    if (plan.variant == TS_VARIANT_FUSED)
-        return hip_status(tsk::launch_fused(a, plan.F, vec, tsk::kFusedProbs, grid, stream));
-    return hip_status(tsk::launch_split(a, plan.F, vec, stream));
+    if (call.plan.variant == TS_VARIANT_FUSED) {
+        int mode = tsk::kFusedProbs;
+        if (group_sums) {
+            mode = tsk::kFusedProbsSums;
+            a.nsub = cdiv(a.V, tsk::kDrawGroup);
+            *sums = true;
+        }
+        return hip_status(tsk::launch_fused(a, call.plan.F, call.vec, mode, call.grid, stream));
+    }
+    return hip_status(tsk::launch_split(a, call.plan.F, call.vec, stream));
 }
 
-// Chunk size for the chunked sampling kernels of a (B, V) call: 4096 columns
-// while the call is small (latency-bound), else 8192 (their LDS holds one
-// transposed chunk, about 37 KiB at 8192); 0 if a row would need more than
-// kSlotStride chunks.
-int chunked_F(int64_t B, int64_t V) {
-    if (B * V <= (int64_t(1) << 21) && cdiv(V, 4096) <= tsk::kSlotStride) return 4;
-    if (cdiv(V, 8192) <= tsk::kSlotStride) return 8;
-    return 0;
+ts_status run_softmax(const float* logits, const float* temps, const uint32_t* allowed, int64_t B, int64_t V,
+                      float* out, int variant, int chunk, hipStream_t stream) {
+    if (!sizes_ok(B, V)) return TS_ERR_INVALID_ARGUMENT;
+    if (B == 0) return TS_OK;
+    SoftmaxCall call;
+    ts_status st = prepare_softmax(logits, temps, allowed, B, V, out, variant, chunk, &call);
+    if (st != TS_OK) return st;
+    if (call.plan.variant == TS_VARIANT_ROWWISE) return launch_softmax(call, WsView{}, false, nullptr, stream);
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace* w = nullptr;
+    st = ws_get(stream, call.need_b, call.need_p, &w);
+    if (st != TS_OK) return st;
+    return launch_softmax(call, ws_view(*w), false, nullptr, stream);
+}
+
+// Groups per workgroup of the draw's partials kernel: enough workgroups to
+// fill the device for large calls, more and smaller ones for small calls.
+int draw_F(int64_t B, int64_t V) {
+    if (B * cdiv(V, 8 * tsk::kDrawGroup) >= 1024) return 8;
+    if (B * cdiv(V, 4 * tsk::kDrawGroup) >= 512) return 4;
+    return 1;
+}
+
+// The draw's two kernels (draw_kernels.hip) on x = logits (kDrawLogits) or
+// probabilities (kDrawProbs); partials_done: the group partials are already in
+// v.part (written by the fused softmax). Called with g_mu held.
+ts_status launch_draw(int kind, const float* x, const float* temps, const uint32_t* allowed, const float* uniforms,
+                      int64_t B, int64_t V, int64_t K, int32_t* out_ids, const WsView& v, bool partials_done,
+                      hipStream_t stream) {
+    tsk::DrawArgs d{};
+    d.x = x;
+    d.temps = temps;
+    d.allowed = allowed;
+    d.mwords = mask_words(V);
+    d.uniforms = uniforms;
+    d.out_ids = out_ids;
+    d.part = v.part;
+    d.B = B;
+    d.V = V;
+    d.K = K;
+    d.nsub = cdiv(V, tsk::kDrawGroup);
+    const bool vec = aligned16(x) && (V % 4 == 0);
+    if (!partials_done) {
+        const int F = draw_F(B, V);
+        d.nch = cdiv(V, tsk::kDrawGroup * F);
+        hipError_t e = tsk::launch_group_partials(d, F, vec, kind, stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(tsk::launch_draw_resolve(d, vec, kind, stream));
+}
+
+// Size limits of the draw's grids (32-bit grid dimensions).
+bool draw_sizes_ok(int64_t B, int64_t V, int64_t K) {
+    return B * cdiv(V, tsk::kDrawGroup) <= INT32_MAX && cdiv(B * K, 4) <= INT32_MAX;
 }
 
 }  // namespace
@@ -319,34 +387,15 @@ TS_API ts_status ts_sample(const float* probs, const float* uniforms, int64_t B,
     if (!sizes_ok(B, V) || K < 0 || (K > 0 && B > (INT64_MAX / 8) / K)) return TS_ERR_INVALID_ARGUMENT;
     if (B == 0 || K == 0) return TS_OK;
     if (!probs || !uniforms || !out_ids) return TS_ERR_INVALID_ARGUMENT;
-    if (B > INT32_MAX) return TS_ERR_INVALID_ARGUMENT;
+    if (!draw_sizes_ok(B, V, K)) return TS_ERR_INVALID_ARGUMENT;
     if (overlaps(out_ids, B * K * 4, probs, B * V * 4) || overlaps(out_ids, B * K * 4, uniforms, B * K * 4))
         return TS_ERR_INVALID_ARGUMENT;
-    tsk::SampleArgs a{};
-    a.probs = probs;
-    a.uniforms = uniforms;
-    a.out_ids = out_ids;
-    a.B = B;
-    a.V = V;
-    a.K = K;
-    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-    const bool vec = aligned16(probs) && (V % 4 == 0);
-    const int F = chunked_F(B, V);
-    if (F == 0) return hip_status(tsk::launch_sample_rows(a, vec, stream));
-    int64_t cap = 0;
-    ts_status st = resident_cap(3, F, vec, &cap);
-    if (st != TS_OK) return st;
-    a.nch = cdiv(V, 1024 * F);
-    a.items = B * a.nch;
-    if (a.nch > cap) return hip_status(tsk::launch_sample_rows(a, vec, stream));
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace* w = nullptr;
-    st = ws_get(stream, B, 0, &w);
+    ts_status st = ws_get(stream, 0, B * cdiv(V, tsk::kDrawGroup), &w);
     if (st != TS_OK) return st;
-    const WsView v = ws_view(*w);
-    a.fslots = v.sets[tsk::kSetFloatSums];
-    a.err = v.err;
-    return hip_status(tsk::launch_sample_chunks(a, F, vec, fused_grid(a.items, a.nch, cap), stream));
+    return launch_draw(tsk::kDrawProbs, probs, nullptr, nullptr, uniforms, B, V, K, out_ids, ws_view(*w), false,
+                       stream);
 }
 
 TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, const uint32_t* allowed,
@@ -370,36 +419,31 @@ TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, cons
         return TS_ERR_INVALID_ARGUMENT;
     if (K == 0)
         return probs_out ? run_softmax(logits, temps, allowed, B, V, probs_out, TS_VARIANT_AUTO, 0, stream) : TS_OK;
-    const int F = chunked_F(B, V);
-    if (F == 0) return TS_ERR_INVALID_ARGUMENT;   // rows longer than kSlotStride * 8192 columns
-    const bool vec = aligned16(logits) && (V % 4 == 0) && (!probs_out || aligned16(probs_out));
-    const int mode = probs_out ? tsk::kFusedProbsIds : tsk::kFusedIds;
-    int64_t cap = 0;
-    ts_status st = resident_cap(mode, F, vec, &cap);
+    if (!draw_sizes_ok(B, V, K)) return TS_ERR_INVALID_ARGUMENT;
+    const int64_t nparts = B * cdiv(V, tsk::kDrawGroup);
+    if (!probs_out) {
+        // ids only: group partials straight from the logits (one read), then the draw
+        std::lock_guard<std::mutex> lk(g_mu);
+        Workspace* w = nullptr;
+        ts_status st = ws_get(stream, 0, nparts, &w);
+        if (st != TS_OK) return st;
+        return launch_draw(tsk::kDrawLogits, logits, temps, allowed, uniforms, B, V, K, out_ids, ws_view(*w), false,
+                           stream);
+    }
+    // probabilities and ids: the softmax (the fused split also leaves the group
+    // sums of the probabilities), then the draw on the written probabilities
+    SoftmaxCall call;
+    ts_status st = prepare_softmax(logits, temps, allowed, B, V, probs_out, TS_VARIANT_AUTO, 0, &call);
     if (st != TS_OK) return st;
-    tsk::SoftmaxArgs a{};
-    a.logits = logits;
-    a.temps = temps;
-    a.allowed = allowed;
-    a.mwords = mask_words(V);
-    a.out = probs_out;
-    a.B = B;
-    a.V = V;
-    a.nch = cdiv(V, 1024 * F);
-    a.items = B * a.nch;
-    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-    a.uniforms = uniforms;
-    a.out_ids = out_ids;
-    a.K = K;
-    if (a.nch > cap) return TS_ERR_INVALID_ARGUMENT;
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace* w = nullptr;
-    st = ws_get(stream, B, 0, &w);
+    st = ws_get(stream, call.need_b, call.need_p > nparts ? call.need_p : nparts, &w);
     if (st != TS_OK) return st;
     const WsView v = ws_view(*w);
-    a.slots = v.sets[tsk::kSetPartials];
-    a.err = v.err;
-    return hip_status(tsk::launch_fused(a, F, vec, mode, fused_grid(a.items, a.nch, cap), stream));
+    bool sums = false;
+    st = launch_softmax(call, v, true, &sums, stream);
+    if (st != TS_OK) return st;
+    return launch_draw(tsk::kDrawProbs, probs_out, nullptr, nullptr, uniforms, B, V, K, out_ids, v, sums, stream);
 }
 
 TS_API ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream) {
