@@ -115,23 +115,30 @@ __global__ __launch_bounds__(DT) void ts_group_partials(DrawArgs a) {
 
 // ---------------------------------------------------------------------------
 // ts_draw_resolve: wave g of the grid draws target g % K of row g / K.
-// Lane l looks at groups b0 + 4 l + [0, 4) of each tile of 256 groups.
+// Lane l looks at groups b0 + 4 l + [0, 4) of each tile of 256 groups. With
+// ONE (a row of at most 256 groups) the lane's 4 partials are loaded once and
+// kept in registers; otherwise each pass reloads them tile by tile.
 // ---------------------------------------------------------------------------
 template <int KIND>
-struct GroupWeight {
+struct GroupWeights {
     const float2* prow;
     int64_t nsub;
     float gsh, k;
-    // the group's share of the row: 0 past the row's end
-    __device__ __forceinline__ float operator()(int64_t i) const {
-        if (i >= nsub) return 0.0f;
-        const float2 v = prow[i];
+    // the 4 weights (shares of the row) of lane `ln` in tile b0: 0 past the row's end
+    __device__ __forceinline__ void tile(int64_t b0, int ln, float (&w)[4]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i = b0 + 4 * ln + e;
+            w[e] = i < nsub ? weight(prow[i]) : 0.0f;
+        }
+    }
+    __device__ __forceinline__ float weight(float2 v) const {
         if constexpr (KIND == kDrawLogits) return masked_term(v.x, v.y * exp2_hw((v.x - gsh) * k));
         else return v.x;
     }
 };
 
-template <int KIND, bool VEC>
+template <int KIND, bool VEC, bool ONE>
 __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     const int ln = threadIdx.x & (kWave - 1);
     const int64_t g = static_cast<int64_t>(blockIdx.x) * DW + threadIdx.x / kWave;
@@ -139,26 +146,53 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     const int64_t row = g / a.K;
     const int64_t nsub = a.nsub;
     constexpr int64_t TILE = 4 * kWave;
-    GroupWeight<KIND> weight{a.part + row * nsub, nsub, 0.0f, 0.0f};
+    GroupWeights<KIND> gw{a.part + row * nsub, nsub, 0.0f, 0.0f};
+    // independent loads first: the uniform, the temperature, the partials
+    const float u = a.uniforms[g];
+    if constexpr (KIND == kDrawLogits) gw.k = exp2_scale(a.temps[row]);
+    float2 pv[4];
+    if constexpr (ONE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i = 4 * ln + e;
+            pv[e] = i < nsub ? gw.prow[i] : make_float2(kNegInf, 0.0f);
+        }
+    }
+    float w[4];   // ONE: the lane's weights, computed once
 
     if constexpr (KIND == kDrawLogits) {
         // the row max of the group maxima, as the finalize takes it
-        weight.k = exp2_scale(a.temps[row]);
         float mm = kNegInf;
-        for (int64_t b0 = 0; b0 < nsub; b0 += TILE)
+        if constexpr (ONE) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t i = b0 + 4 * ln + e;
-                if (i < nsub) mm = fmaxf(mm, weight.prow[i].x);
-            }
-        weight.gsh = guarded_shift(wave_reduce<MaxOp>(mm));
+            for (int e = 0; e < 4; ++e) mm = fmaxf(mm, pv[e].x);
+        } else {
+            for (int64_t b0 = 0; b0 < nsub; b0 += TILE)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t i = b0 + 4 * ln + e;
+                    if (i < nsub) mm = fmaxf(mm, gw.prow[i].x);
+                }
+        }
+        gw.gsh = guarded_shift(wave_reduce<MaxOp>(mm));
+    }
+    if constexpr (ONE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = 4 * ln + e < nsub ? gw.weight(pv[e]) : 0.0f;
     }
 
     // float total of the weights (fixed order) -> the scale of the integer weights
     float tl = 0.0f;
-    for (int64_t b0 = 0; b0 < nsub; b0 += TILE)
+    if constexpr (ONE) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tl += weight(b0 + 4 * ln + e);
+        for (int e = 0; e < 4; ++e) tl += w[e];
+    } else {
+        for (int64_t b0 = 0; b0 < nsub; b0 += TILE) {
+            gw.tile(b0, ln, w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tl += w[e];
+        }
+    }
     const float tot = wave_reduce<SumOp>(tl);
     int32_t* out = a.out_ids + g;
     if (!(tot > 0.0f) || !(tot < __builtin_huge_valf())) {   // nothing can be drawn
@@ -167,20 +201,28 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     }
     const int s = scale_exponent(tot);
     uint64_t ql = 0;
-    for (int64_t b0 = 0; b0 < nsub; b0 += TILE)
+    if constexpr (ONE) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ql += fixed_point(weight(b0 + 4 * ln + e), s);
+        for (int e = 0; e < 4; ++e) ql += fixed_point(w[e], s);
+    } else {
+        for (int64_t b0 = 0; b0 < nsub; b0 += TILE) {
+            gw.tile(b0, ln, w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ql += fixed_point(w[e], s);
+        }
+    }
     const uint64_t Q = wave_sum_u64(ql);
-    const uint64_t T = target_of(a.uniforms[g], Q);
+    const uint64_t T = target_of(u, Q);
 
     // the group whose integer range [P, P + q) holds T
     int64_t m = 0;
     uint64_t Pm = 0, qm = 0, carry = 0;
     for (int64_t b0 = 0; b0 < nsub; b0 += TILE) {
+        if constexpr (!ONE) gw.tile(b0, ln, w);
         uint64_t q[4], lsum = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            q[e] = fixed_point(weight(b0 + 4 * ln + e), s);
+            q[e] = fixed_point(w[e], s);
             lsum += q[e];
         }
         const uint64_t incl = wave_inclusive_scan_u64(lsum);
@@ -240,12 +282,12 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
                 if (col0 + i < a.V && !((bits >> i) & 1u)) v[i] = kNegInf;
         }
         // e = exp2((x - shift) k) <= 1 at the group's own max (the partial's pm)
-        const float sh = guarded_shift(weight.prow[m].x);
+        const float sh = guarded_shift(gw.prow[m].x);
 #pragma unroll
-        for (int i = 0; i < GL; ++i) v[i] = exp2_hw((v[i] - sh) * weight.k);
+        for (int i = 0; i < GL; ++i) v[i] = exp2_hw((v[i] - sh) * gw.k);
         se = 61 - 10;   // 1024 entries <= 1: integer total <= 2^61
     } else {
-        se = scale_exponent(weight.prow[m].x);   // > 0: the group's q weight is >= 1
+        se = scale_exponent(gw.prow[m].x);   // > 0: the group's q weight is >= 1
     }
     uint64_t gsum = 0;
 #pragma unroll
@@ -287,17 +329,20 @@ hipError_t launch_group_partials(const DrawArgs& a, int F, bool vec, int kind, h
     }
 }
 
+template <int KIND, bool ONE>
+hipError_t resolve_impl(const DrawArgs& a, bool vec, dim3 grid, hipStream_t s) {
+    if (vec) hipLaunchKernelGGL((ts_draw_resolve<KIND, true, ONE>), grid, dim3(DT), 0, s, a);
+    else hipLaunchKernelGGL((ts_draw_resolve<KIND, false, ONE>), grid, dim3(DT), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_draw_resolve(const DrawArgs& a, bool vec, int kind, hipStream_t s) {
     const int64_t waves = a.B * a.K;
     const dim3 grid(static_cast<uint32_t>((waves + DW - 1) / DW));
-    if (kind == kDrawLogits) {
-        if (vec) hipLaunchKernelGGL((ts_draw_resolve<kDrawLogits, true>), grid, dim3(DT), 0, s, a);
-        else hipLaunchKernelGGL((ts_draw_resolve<kDrawLogits, false>), grid, dim3(DT), 0, s, a);
-    } else {
-        if (vec) hipLaunchKernelGGL((ts_draw_resolve<kDrawProbs, true>), grid, dim3(DT), 0, s, a);
-        else hipLaunchKernelGGL((ts_draw_resolve<kDrawProbs, false>), grid, dim3(DT), 0, s, a);
-    }
-    return hipGetLastError();
+    const bool one = a.nsub <= 4 * kWave;
+    if (kind == kDrawLogits)
+        return one ? resolve_impl<kDrawLogits, true>(a, vec, grid, s) : resolve_impl<kDrawLogits, false>(a, vec, grid, s);
+    return one ? resolve_impl<kDrawProbs, true>(a, vec, grid, s) : resolve_impl<kDrawProbs, false>(a, vec, grid, s);
 }
 
 }  // namespace tsk

@@ -40,11 +40,11 @@ __device__ __forceinline__ uint64_t target_of(float u, uint64_t Q) {
     return T < Q ? T : Q - 1;
 }
 
-// Sum over the 64 lanes of a wave, returned to every lane.
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
+// Lane `src`'s value of a 64-bit variable, on every lane (src wave-uniform).
+__device__ __forceinline__ uint64_t lane_value_u64(uint64_t v, int src) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), src);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), src);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // Inclusive prefix sum over the lanes of a wave, in lane order.
@@ -58,11 +58,11 @@ __device__ __forceinline__ uint64_t wave_inclusive_scan_u64(uint64_t v) {
     return v;
 }
 
-// Lane `src`'s value of a 64-bit variable, on every lane (src wave-uniform).
-__device__ __forceinline__ uint64_t lane_value_u64(uint64_t v, int src) {
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), src);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), src);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
+// Sum over the 64 lanes of a wave, returned to every lane.
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
 }
 
 }  // namespace tsk
