@@ -22,6 +22,7 @@
 #include "ts_device.h"
 #include "ts_exchange.h"
 #include "ts_launch.h"
+#include "ts_sample_device.h"
 
 namespace tsk {
 
@@ -113,10 +114,9 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 // either costs microseconds per workgroup on a multi-XCD part). The host
 // launches no more workgroups than the device holds at once and at least nch.
 //
-// MODE kFusedProbs writes the probabilities; kFusedProbsSums also writes, per
-// group of kDrawGroup columns (group j of a chunk = lane float4s j NT + t),
-// the sum of its probabilities, for a token draw that follows
-// (draw_kernels.hip).
+// MODE kFusedProbs writes the probabilities; kFusedProbsSums also writes the
+// sums of the probabilities per group of 4096 columns and per block of 64, for
+// a token draw that follows (draw_kernels.hip).
 // ---------------------------------------------------------------------------
 template <int F>
 struct FusedOcc {
@@ -126,9 +126,9 @@ struct FusedOcc {
 
 template <int F, bool VEC, int MODE>
 __global__ __launch_bounds__(NT, (FusedOcc<F>::waves_per_eu)) void ts_fused(SoftmaxArgs a) {
-    static_assert(NT * 4 == kDrawGroup, "a chunk group is one draw group");
+    static_assert(MODE != kFusedProbsSums || F % 4 == 0, "draw sums need whole 4096-column groups");
     __shared__ float red[NW];
-    __shared__ float gsum[MODE == kFusedProbsSums ? F : 1][NW];
+    __shared__ float gsum[MODE == kFusedProbsSums ? (F >= 4 ? F / 4 : 1) : 1][NW];
     __shared__ float chunk_scale;
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
@@ -210,18 +210,24 @@ __global__ __launch_bounds__(NT, (FusedOcc<F>::waves_per_eu)) void ts_fused(Soft
         for (int i = 0; i < 4 * F; ++i) x[i] *= scale;    // the probabilities
         store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
         if constexpr (MODE == kFusedProbsSums) {
+            // the draw's group and block sums of the probabilities just written
+            // (the same sums the draw's partials kernel forms from them)
+            constexpr int NG = F / 4;   // draw groups per chunk
             const int ln = lane & (kWave - 1), wv = lane / kWave;
 #pragma unroll
-            for (int j = 0; j < F; ++j) {
-                const float ws = wave_reduce<SumOp>((x[4 * j] + x[4 * j + 1]) + (x[4 * j + 2] + x[4 * j + 3]));
-                if (ln == 0) gsum[j][wv] = ws;
+            for (int d = 0; d < NG; ++d) {
+                const int64_t G = c * NG + d;
+                float h = 0.0f;
+                if (G < a.ngroups) h = prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup);
+                const float ws = wave_reduce<SumOp>(h);
+                if (ln == 0) gsum[d][wv] = ws;
             }
             __syncthreads();
-            if (lane < F && c * F + lane < a.nsub) {
+            if (lane < NG && c * NG + lane < a.ngroups) {
                 float gs = gsum[lane][0];
 #pragma unroll
                 for (int w = 1; w < NW; ++w) gs += gsum[lane][w];
-                a.part[row * a.nsub + c * F + lane] = make_float2(gs, 0.0f);
+                a.part[row * a.ngroups + c * NG + lane] = make_float2(gs, 0.0f);
             }
         }
 #pragma unroll
@@ -317,8 +323,13 @@ hipError_t split_impl(const SoftmaxArgs& a, hipStream_t s) {
 template <int F, bool VEC>
 hipError_t fused_impl(const SoftmaxArgs& a, int mode, int64_t grid, hipStream_t s) {
     const dim3 g(static_cast<uint32_t>(grid));
-    if (mode == kFusedProbs) hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbs>), g, dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbsSums>), g, dim3(NT), 0, s, a);
+    if (mode == kFusedProbs) {
+        hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbs>), g, dim3(NT), 0, s, a);
+    } else if constexpr (F % 4 == 0) {
+        hipLaunchKernelGGL((ts_fused<F, VEC, kFusedProbsSums>), g, dim3(NT), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -329,8 +340,11 @@ hipError_t fused_cap_impl(int mode, int64_t* cap) {
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const void* fn = mode == kFusedProbs ? reinterpret_cast<const void*>(&ts_fused<F, VEC, kFusedProbs>)
-                                         : reinterpret_cast<const void*>(&ts_fused<F, VEC, kFusedProbsSums>);
+    const void* fn = reinterpret_cast<const void*>(&ts_fused<F, VEC, kFusedProbs>);
+    if (mode != kFusedProbs) {
+        if constexpr (F % 4 == 0) fn = reinterpret_cast<const void*>(&ts_fused<F, VEC, kFusedProbsSums>);
+        else return hipErrorInvalidValue;
+    }
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0);
     if (e != hipSuccess) return e;
     *cap = static_cast<int64_t>(per_cu) * cus;

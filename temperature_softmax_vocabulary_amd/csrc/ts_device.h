@@ -82,6 +82,18 @@ __device__ __forceinline__ float wave_reduce(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Reduction over each row of 16 lanes (lanes 16 r .. 16 r + 15), returned to
+// all 16 lanes of the row: the first four steps of wave_reduce.
+template <class Op>
+__device__ __forceinline__ float row16_reduce(float v) {
+    Op op;
+    v = op(v, dpp_or<0xB1>(v, Op::identity));          // quad_perm [1,0,3,2]
+    v = op(v, dpp_or<0x4E>(v, Op::identity));          // quad_perm [2,3,0,1]
+    v = op(v, dpp_or<0x141>(v, Op::identity));         // row_half_mirror
+    v = op(v, dpp_or<0x140>(v, Op::identity));         // row_mirror
+    return v;
+}
+
 // Workgroup reduction: wave64 DPP reduce, then a fixed-order combine of the
 // NW wave results through LDS. The order never depends on timing, so results
 // are bitwise reproducible. `lds` holds NW floats; the trailing barrier lets

@@ -20,9 +20,12 @@ constexpr int64_t kSlotStride = 256;
 constexpr int kSlotSets = 1;
 constexpr int kSetPartials = 0;
 
-// Token draws work on groups of kDrawGroup columns (one float4 per lane of a
-// 256-lane workgroup): per-group partials, then one wave per target.
-constexpr int kDrawGroup = 1024;
+// Token draws (draw_kernels.hip) work on blocks of kDrawBlock columns and
+// groups of kDrawGroup columns (64 blocks): float partials per group and per
+// block, then one wave per target.
+constexpr int kDrawBlock = 64;
+constexpr int kDrawGroup = 4096;
+constexpr int kBlocksPerGroup = kDrawGroup / kDrawBlock;
 
 // Largest row the resident one-workgroup-per-row kernel holds in registers.
 constexpr int kRowwiseThreads = 1024;
@@ -38,16 +41,18 @@ struct SoftmaxArgs {
     int64_t V;
     int64_t nch;           // chunks per row (split, fused)
     int64_t items;         // B * nch
-    float2* part;          // split: [B * nch] chunk partials (pm, pl);
-                           // fused with group sums: [B * nsub] (sum of probs, 0) per group
-    int64_t nsub;          // groups of kDrawGroup columns per row (fused with group sums)
+    float2* part;          // split: [B * nch] chunk partials (pm, pl); fused with
+                           // draw sums: [B * ngroups] (sum of probs, 0) per group
+    float2* bpart;         // fused with draw sums: [B * ngroups * 64] (sum of probs, 0) per block
+    int64_t ngroups;       // groups of kDrawGroup columns per row (fused with draw sums)
     unsigned long long* slots;   // [B * kSlotStride] tagged (pm, pl) slots of the fused kernel
     uint32_t* err;         // device error flags (bit 0: a bounded wait ran out)
     uint32_t spin_limit;   // polls before a fused wait gives up
 };
 
-// Fused kernel modes: probabilities only; probabilities and the per-group sums
-// of the probabilities (for a token draw that follows).
+// Fused kernel modes: probabilities only; probabilities and the group and
+// block sums of the probabilities (for a token draw that follows; chunks of a
+// whole number of groups, F in {4, 8, 16}).
 constexpr int kFusedProbs = 0, kFusedProbsSums = 1;
 
 hipError_t launch_split(const SoftmaxArgs& a, int F, bool vec, hipStream_t s);
@@ -65,18 +70,17 @@ struct DrawArgs {
     int64_t mwords;
     const float* uniforms;    // [B, K]
     int32_t* out_ids;         // [B, K]
-    float2* part;             // [B, nsub] group partials: (max, sum exp2) or (positive sum, 0)
+    float2* gpart;            // [B, ngroups] group partials: (max, sum exp2) or (positive sum, 0)
+    float2* bpart;            // [B, ngroups, 64] block partials, same pairs
     int64_t B;
     int64_t V;
     int64_t K;
-    int64_t nsub;             // ceil(V / kDrawGroup)
-    int64_t nch;              // workgroups per row of the partials kernel: ceil(V / (kDrawGroup F))
+    int64_t ngroups;          // ceil(V / kDrawGroup)
 };
-// Per-group partials over the whole of x (one read), F groups per workgroup.
-hipError_t launch_group_partials(const DrawArgs& a, int F, bool vec, int kind, hipStream_t s);
-// One wave per (row, target): integer CDF over the row's groups, then the
-// group that holds the target resolves it exactly.
-hipError_t launch_draw_resolve(const DrawArgs& a, bool vec, int kind, hipStream_t s);
+// Group and block partials over the whole of x (one read), one group per workgroup.
+hipError_t launch_draw_partials(const DrawArgs& a, bool vec, int kind, hipStream_t s);
+// One wave per (row, target): the target's group, then its block, then its id.
+hipError_t launch_draw_resolve(const DrawArgs& a, int kind, hipStream_t s);
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, bool vec, hipStream_t s);
 

@@ -65,4 +65,29 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
     return v;
 }
 
+// Block sums of probabilities for one group of a chunk held in the layout of
+// load_chunk with 256 lanes: the group is the four 1024-column chunk groups
+// j0 .. j0 + 3, and block b = 16 (j - j0) + t / 16 is the 4 entries of each of
+// the 16 lanes of one row of lanes. Writes (sum, 0) of every block to bgroup[b]
+// from the row's last lane and returns that lane's share of the group sum (0
+// on the other lanes). Both the fused softmax (on the probabilities it writes)
+// and the draw's partials kernel (on given probabilities) sum this way, so the
+// same probabilities give the same sums.
+template <int F>
+__device__ __forceinline__ float prob_block_sums(const float (&p)[4 * F], int j0, float2* __restrict__ bgroup) {
+    const int t = threadIdx.x;
+    const bool holder = (t & 15) == 15;
+    float bs[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int j = j0 + jj;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = p[4 * j + e] > 0.0f ? p[4 * j + e] : 0.0f;
+        bs[jj] = row16_reduce<SumOp>((y[0] + y[1]) + (y[2] + y[3]));
+        if (holder) bgroup[jj * 16 + (t >> 4)] = make_float2(bs[jj], 0.0f);
+    }
+    return holder ? (bs[0] + bs[1]) + (bs[2] + bs[3]) : 0.0f;
+}
+
 }  // namespace tsk

@@ -288,9 +288,10 @@ ts_status launch_softmax(SoftmaxCall& call, const WsView& v, bool group_sums, bo
     a.err = v.err;
     if (call.plan.variant == TS_VARIANT_FUSED) {
         int mode = tsk::kFusedProbs;
-        if (group_sums) {
+        if (group_sums && call.plan.F % 4 == 0) {   // chunks of whole draw groups
             mode = tsk::kFusedProbsSums;
-            a.nsub = cdiv(a.V, tsk::kDrawGroup);
+            a.ngroups = cdiv(a.V, tsk::kDrawGroup);
+            a.bpart = v.part + a.B * a.ngroups;
             *sums = true;
         }
         return hip_status(tsk::launch_fused(a, call.plan.F, call.vec, mode, call.grid, stream));
@@ -313,17 +314,13 @@ ts_status run_softmax(const float* logits, const float* temps, const uint32_t* a
     return launch_softmax(call, ws_view(*w), false, nullptr, stream);
 }
 
-// Groups per workgroup of the draw's partials kernel: enough workgroups to
-// fill the device for large calls, more and smaller ones for small calls.
-int draw_F(int64_t B, int64_t V) {
-    if (B * cdiv(V, 8 * tsk::kDrawGroup) >= 1024) return 8;
-    if (B * cdiv(V, 4 * tsk::kDrawGroup) >= 512) return 4;
-    return 1;
-}
+// Workspace partials of a draw: per row, one per group of 4096 columns, then
+// 64 per group (its blocks of 64 columns).
+int64_t draw_parts(int64_t B, int64_t V) { return B * cdiv(V, tsk::kDrawGroup) * (1 + tsk::kBlocksPerGroup); }
 
 // The draw's two kernels (draw_kernels.hip) on x = logits (kDrawLogits) or
-// probabilities (kDrawProbs); partials_done: the group partials are already in
-// v.part (written by the fused softmax). Called with g_mu held.
+// probabilities (kDrawProbs); partials_done: the partials are already in the
+// workspace (written by the fused softmax). Called with g_mu held.
 ts_status launch_draw(int kind, const float* x, const float* temps, const uint32_t* allowed, const float* uniforms,
                       int64_t B, int64_t V, int64_t K, int32_t* out_ids, const WsView& v, bool partials_done,
                       hipStream_t stream) {
@@ -334,19 +331,18 @@ ts_status launch_draw(int kind, const float* x, const float* temps, const uint32
     d.mwords = mask_words(V);
     d.uniforms = uniforms;
     d.out_ids = out_ids;
-    d.part = v.part;
     d.B = B;
     d.V = V;
     d.K = K;
-    d.nsub = cdiv(V, tsk::kDrawGroup);
+    d.ngroups = cdiv(V, tsk::kDrawGroup);
+    d.gpart = v.part;
+    d.bpart = v.part + B * d.ngroups;
     const bool vec = aligned16(x) && (V % 4 == 0);
     if (!partials_done) {
-        const int F = draw_F(B, V);
-        d.nch = cdiv(V, tsk::kDrawGroup * F);
-        hipError_t e = tsk::launch_group_partials(d, F, vec, kind, stream);
+        hipError_t e = tsk::launch_draw_partials(d, vec, kind, stream);
         if (e != hipSuccess) return hip_status(e);
     }
-    return hip_status(tsk::launch_draw_resolve(d, vec, kind, stream));
+    return hip_status(tsk::launch_draw_resolve(d, kind, stream));
 }
 
 // Size limits of the draw's grids (32-bit grid dimensions).
@@ -392,7 +388,7 @@ TS_API ts_status ts_sample(const float* probs, const float* uniforms, int64_t B,
         return TS_ERR_INVALID_ARGUMENT;
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace* w = nullptr;
-    ts_status st = ws_get(stream, 0, B * cdiv(V, tsk::kDrawGroup), &w);
+    ts_status st = ws_get(stream, 0, draw_parts(B, V), &w);
     if (st != TS_OK) return st;
     return launch_draw(tsk::kDrawProbs, probs, nullptr, nullptr, uniforms, B, V, K, out_ids, ws_view(*w), false,
                        stream);
@@ -420,7 +416,7 @@ TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, cons
     if (K == 0)
         return probs_out ? run_softmax(logits, temps, allowed, B, V, probs_out, TS_VARIANT_AUTO, 0, stream) : TS_OK;
     if (!draw_sizes_ok(B, V, K)) return TS_ERR_INVALID_ARGUMENT;
-    const int64_t nparts = B * cdiv(V, tsk::kDrawGroup);
+    const int64_t nparts = draw_parts(B, V);
     if (!probs_out) {
         // ids only: group partials straight from the logits (one read), then the draw
         std::lock_guard<std::mutex> lk(g_mu);
@@ -450,7 +446,9 @@ TS_API ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream) {
     if (!sizes_ok(max_B, max_V)) return TS_ERR_INVALID_ARGUMENT;
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace* w = nullptr;
-    return ws_get(stream, max_B, max_B * cdiv(max_V, tsk::kMinChunk), &w);
+    const int64_t split_parts = max_B * cdiv(max_V, tsk::kMinChunk);
+    const int64_t parts = draw_parts(max_B, max_V);
+    return ws_get(stream, max_B, split_parts > parts ? split_parts : parts, &w);
 }
 
 TS_API ts_status ts_device_errors(hipStream_t stream, uint32_t* flags) {
