@@ -46,25 +46,56 @@ __device__ __forceinline__ const uint32_t* draw_mask_row(const DrawArgs& a, int6
     return a.allowed ? a.allowed + row * a.mwords : nullptr;
 }
 
+// N sums (or maxima) over the workgroup at once: one LDS round for all of
+// them, combined in a fixed order; every lane gets every result.
+template <class Op, int NW, int N>
+__device__ __forceinline__ void block_reduce_n(float (&v)[N], float (*lds)[NW]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float w = wave_reduce<Op>(v[i]);
+        if ((threadIdx.x & (kWave - 1)) == 0) lds[i][threadIdx.x / kWave] = w;
+    }
+    __syncthreads();
+    Op op;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float r = lds[i][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = op(r, lds[i][w]);
+        v[i] = r;
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
-// ts_draw_partials: workgroup (row, G) reads group G in the layout of
-// load_chunk (F = 4: chunk group j = columns G 4096 + j 1024 + [0, 1024), lane
-// t holding 4 consecutive columns of each), so block b = 16 j + t / 16 is one
-// row of 16 lanes.
+// ts_draw_partials: workgroup (row, h) reads groups G = GPW h + d, d < GPW, in
+// the layout of load_chunk (F = 4 GPW: chunk group j = columns
+// GPW h 4096 + j 1024 + [0, 1024), lane t holding 4 consecutive columns of
+// each), so group G = GPW h + j / 4 and its block b = 16 (j % 4) + t / 16 is
+// one row of 16 lanes.
 // ---------------------------------------------------------------------------
-template <bool VEC, int KIND>
+template <bool VEC, int KIND, int GPW>
 __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
-    __shared__ float red[DW];
-    constexpr int F = 4;
+    __shared__ float red[GPW][DW];   // (logits only)
+    constexpr int F = 4 * GPW;
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x / a.ngroups;
-    const int64_t G = blockIdx.x - row * a.ngroups;
-    float2* bgroup = a.bpart + (row * a.ngroups + G) * kBlocksPerGroup;
+    const int64_t nh = (a.ngroups + GPW - 1) / GPW;
+    const int64_t row = blockIdx.x / nh;
+    const int64_t h = blockIdx.x - row * nh;
+    const int64_t G0 = h * GPW;
+    const bool holder = (t & 15) == 15;
     float x[4 * F];
     if constexpr (KIND == kDrawLogits) {
-        load_chunk<DT, F, VEC, true>(a.x + row * a.V, G * kDrawGroup, a.V, x, kNegInf, draw_mask_row(a, row));
+        {
+            const int64_t c0 = G0 * kDrawGroup;
+            const uint32_t* mrow = draw_mask_row(a, row);
+            uint32_t mw[2];
+            issue_chunk_loads<DT, F, VEC, true>(a.x + row * a.V, c0, a.V, x);
+            if (mrow) load_mask_words<DT, F>(mrow, c0, a.V, mw);
+            fill_past_end<DT, F>(c0, a.V, x, kNegInf);
+            if (mrow) apply_mask_words<DT, F>(c0, a.V, mw, x);
+        }
         const float k = exp2_scale(a.temps[row]);
-        const bool holder = (t & 15) == 15;
         float bm[F], bl[F];
 #pragma unroll
         for (int j = 0; j < F; ++j) {
@@ -74,21 +105,53 @@ __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) l[e] = exp2_hw((x[4 * j + e] - sh) * k);
             bl[j] = row16_reduce<SumOp>((l[0] + l[1]) + (l[2] + l[3]));
-            if (holder) bgroup[j * 16 + (t >> 4)] = make_float2(bm[j], bl[j]);
         }
-        // the group: max of the block maxima, and the blocks' sums rescaled to it
-        const float gm = block_reduce<MaxOp, DW>(fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3])), red);
-        const float gsh = guarded_shift(gm);
-        float gl = 0.0f;
-        if (holder)
+        // each group: max of its block maxima, and its blocks' sums rescaled to it
+        float gm[GPW], gl[GPW];
 #pragma unroll
-            for (int j = 0; j < F; ++j) gl += masked_term(bm[j], bl[j] * exp2_hw((bm[j] - gsh) * k));
-        gl = block_reduce<SumOp, DW>(gl, red);
-        if (t == 0) a.gpart[row * a.ngroups + G] = make_float2(gm, gl);
+        for (int d = 0; d < GPW; ++d)
+            gm[d] = fmaxf(fmaxf(bm[4 * d], bm[4 * d + 1]), fmaxf(bm[4 * d + 2], bm[4 * d + 3]));
+        block_reduce_n<MaxOp, DW, GPW>(gm, red);
+#pragma unroll
+        for (int d = 0; d < GPW; ++d) {
+            const float gsh = guarded_shift(gm[d]);
+            gl[d] = 0.0f;
+            if (holder)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 4 * d + jj;
+                    gl[d] += masked_term(bm[j], bl[j] * exp2_hw((bm[j] - gsh) * k));
+                }
+        }
+        block_reduce_n<SumOp, DW, GPW>(gl, red);
+#pragma unroll
+        for (int d = 0; d < GPW; ++d) {
+            const int64_t G = G0 + d;
+            if (G >= a.ngroups) break;
+            if (holder) {
+                float2* bgroup = a.bpart + (row * a.ngroups + G) * kBlocksPerGroup;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) bgroup[jj * 16 + (t >> 4)] = make_float2(bm[4 * d + jj], bl[4 * d + jj]);
+            }
+            if (t == 0) a.gpart[row * a.ngroups + G] = make_float4(gm[d], gl[d], 0.0f, 0.0f);
+        }
     } else {
-        load_chunk<DT, F, VEC, true>(a.x + row * a.V, G * kDrawGroup, a.V, x, 0.0f);
-        const float gs = block_reduce<SumOp, DW>(prob_block_sums<F>(x, 0, bgroup), red);
-        if (t == 0) a.gpart[row * a.ngroups + G] = make_float2(gs, 0.0f);
+        issue_chunk_loads<DT, F, VEC, true>(a.x + row * a.V, G0 * kDrawGroup, a.V, x);
+        fill_past_end<DT, F>(G0 * kDrawGroup, a.V, x, 0.0f);
+        float gs[GPW];
+#pragma unroll
+        for (int d = 0; d < GPW; ++d) {
+            const int64_t G = G0 + d;   // (workgroup-uniform test: a group past the row's end writes nothing)
+            gs[d] = G < a.ngroups ? prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup)
+                                  : 0.0f;
+        }
+        // each wave's share of each group sum (kernel-wide no barrier)
+#pragma unroll
+        for (int d = 0; d < GPW; ++d) {
+            const float w = wave_reduce<SumOp>(gs[d]);
+            if ((t & (kWave - 1)) == 0 && G0 + d < a.ngroups)
+                reinterpret_cast<float*>(a.gpart + row * a.ngroups + G0 + d)[t / kWave] = w;
+        }
     }
 }
 
@@ -96,13 +159,11 @@ __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
 // ts_draw_resolve: wave w of the grid draws target w % K of row w / K.
 // ---------------------------------------------------------------------------
 
-// The lane whose integer range [lo, lo + q) holds T, with lo the lane's
-// exclusive prefix plus `base`; -1 if none. Wave-uniform.
-__device__ __forceinline__ int find_lane(uint64_t q, uint64_t base, uint64_t T, uint64_t* incl_out) {
-    const uint64_t incl = wave_inclusive_scan_u64(q);
+// The lane whose integer range [base + incl - q, base + incl) holds T (incl:
+// the lane's inclusive prefix of q); -1 if none. Wave-uniform.
+__device__ __forceinline__ int find_lane(uint64_t q, uint64_t incl, uint64_t base, uint64_t T) {
     const uint64_t lo = base + incl - q;
     const bool hit = T >= lo && T - lo < q;
-    *incl_out = incl;
     const uint64_t hits = __ballot(hit);
     return hits ? __ffsll(static_cast<unsigned long long>(hits)) - 1 : -1;
 }
@@ -122,24 +183,24 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     if (wid >= a.B * a.K) return;   // the whole wave
     const int64_t row = wid / a.K;
     const int64_t ng = a.ngroups;
-    const float2* grow = a.gpart + row * ng;
+    const float4* grow = a.gpart + row * ng;
     int32_t* out = a.out_ids + wid;
     // independent loads first
     const float u = a.uniforms[wid];
     const float k = KIND == kDrawLogits ? exp2_scale(a.temps[row]) : 0.0f;
 
     // level 1: the row's groups, 64 per tile, lane l holding group b0 + l
-    const float2 gv = ln < ng ? grow[ln] : make_float2(kNegInf, 0.0f);
+    const float4 gv = ln < ng ? grow[ln] : make_float4(kNegInf, 0.0f, 0.0f, 0.0f);
     float gsh = 0.0f;
     if constexpr (KIND == kDrawLogits) {
         float mm = gv.x;
         for (int64_t b0 = kWave; b0 < ng; b0 += kWave) mm = fmaxf(mm, b0 + ln < ng ? grow[b0 + ln].x : kNegInf);
         gsh = guarded_shift(wave_reduce<MaxOp>(mm));
     }
-    auto group_weight = [&](float2 v, int64_t i) -> float {
+    auto group_weight = [&](float4 v, int64_t i) -> float {
         if (i >= ng) return 0.0f;
         if constexpr (KIND == kDrawLogits) return masked_term(v.x, v.y * exp2_hw((v.x - gsh) * k));
-        else return v.x;
+        else return group_prob_sum(v);
     };
     const float gw0 = group_weight(gv, ln);
     float tl = gw0;
@@ -152,18 +213,24 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     }
     const int s1 = scale_exponent(tot);
     const uint64_t q0 = fixed_point(gw0, s1);
-    uint64_t ql = q0;
-    for (int64_t b0 = kWave; b0 < ng; b0 += kWave)
-        ql += b0 + ln < ng ? fixed_point(group_weight(grow[b0 + ln], b0 + ln), s1) : 0;
-    const uint64_t Q = wave_sum_u64(ql);
+    const uint64_t incl0 = wave_inclusive_scan_u64(q0);
+    uint64_t Q = lane_value_u64(incl0, kWave - 1);
+    if (ng > kWave) {   // the row's integer total over every tile
+        uint64_t ql = 0;
+        for (int64_t b0 = kWave; b0 < ng; b0 += kWave)
+            ql += b0 + ln < ng ? fixed_point(group_weight(grow[b0 + ln], b0 + ln), s1) : 0;
+        Q += wave_sum_u64(ql);
+    }
     const uint64_t T = target_of(u, Q);
     int64_t G = -1;
     uint64_t PG = 0, qG = 0, carry = 0;
     for (int64_t b0 = 0; b0 < ng; b0 += kWave) {
-        const uint64_t q = b0 == 0 ? q0
-                           : (b0 + ln < ng ? fixed_point(group_weight(grow[b0 + ln], b0 + ln), s1) : 0);
-        uint64_t incl;
-        const int src = find_lane(q, carry, T, &incl);
+        uint64_t q = q0, incl = incl0;
+        if (b0 > 0) {
+            q = b0 + ln < ng ? fixed_point(group_weight(grow[b0 + ln], b0 + ln), s1) : 0;
+            incl = wave_inclusive_scan_u64(q);
+        }
+        const int src = find_lane(q, incl, carry, T);
         if (src >= 0) {
             G = b0 + src;
             PG = carry + lane_value_u64(incl - q, src);
@@ -191,10 +258,9 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     }
     const int s2 = scale_exponent(wave_reduce<SumOp>(bw));   // > 0: qG >= 1 needs a positive group
     const uint64_t qb = fixed_point(bw, s2);
-    uint64_t incl2;
-    const uint64_t Q2 = wave_sum_u64(qb);
-    const uint64_t T2 = carry_target(T, PG, qG, Q2);
-    const int b = find_lane(qb, 0, T2, &incl2);
+    const uint64_t incl2 = wave_inclusive_scan_u64(qb);
+    const uint64_t T2 = carry_target(T, PG, qG, lane_value_u64(incl2, kWave - 1));
+    const int b = find_lane(qb, incl2, 0, T2);
     if (b < 0) {
         if (ln == 0) *out = -1;
         return;
@@ -218,26 +284,31 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
         s3 = scale_exponent(bx);                     // > 0: the block was chosen
     }
     const uint64_t qe = fixed_point(v, s3);
-    const uint64_t Q3 = wave_sum_u64(qe);
-    const uint64_t T3 = carry_target(T2, Pb, qbb, Q3);
-    uint64_t incl3;
-    const int e = find_lane(qe, 0, T3, &incl3);
+    const uint64_t incl3 = wave_inclusive_scan_u64(qe);
+    const uint64_t T3 = carry_target(T2, Pb, qbb, lane_value_u64(incl3, kWave - 1));
+    const int e = find_lane(qe, incl3, 0, T3);
     if (e < 0 && ln == 0) *out = -1;
     if (ln == e) *out = static_cast<int32_t>(col);
 }
 
-template <bool VEC>
+// Groups per workgroup of the partials kernel: two (32 KiB of reads) once the
+// call fills the device, else one.
+constexpr int kPartialsGPW = 2;
+
+template <bool VEC, int GPW>
 hipError_t partials_impl(const DrawArgs& a, int kind, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(a.B * a.ngroups));
-    if (kind == kDrawLogits) hipLaunchKernelGGL((ts_draw_partials<VEC, kDrawLogits>), grid, dim3(DT), 0, s, a);
-    else hipLaunchKernelGGL((ts_draw_partials<VEC, kDrawProbs>), grid, dim3(DT), 0, s, a);
+    const dim3 grid(static_cast<uint32_t>(a.B * ((a.ngroups + GPW - 1) / GPW)));
+    if (kind == kDrawLogits) hipLaunchKernelGGL((ts_draw_partials<VEC, kDrawLogits, GPW>), grid, dim3(DT), 0, s, a);
+    else hipLaunchKernelGGL((ts_draw_partials<VEC, kDrawProbs, GPW>), grid, dim3(DT), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_draw_partials(const DrawArgs& a, bool vec, int kind, hipStream_t s) {
-    return vec ? partials_impl<true>(a, kind, s) : partials_impl<false>(a, kind, s);
+    const bool wide = a.B * a.ngroups >= 2048;
+    if (wide) return vec ? partials_impl<true, kPartialsGPW>(a, kind, s) : partials_impl<false, kPartialsGPW>(a, kind, s);
+    return vec ? partials_impl<true, 1>(a, kind, s) : partials_impl<false, 1>(a, kind, s);
 }
 
 hipError_t launch_draw_resolve(const DrawArgs& a, int kind, hipStream_t s) {

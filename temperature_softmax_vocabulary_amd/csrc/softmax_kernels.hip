@@ -118,17 +118,18 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 // sums of the probabilities per group of 4096 columns and per block of 64, for
 // a token draw that follows (draw_kernels.hip).
 // ---------------------------------------------------------------------------
-template <int F>
+template <int F, int MODE>
 struct FusedOcc {
-    // registers hold the current and the next chunk (8 F floats per lane)
-    static constexpr int waves_per_eu = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
+    // registers hold the current and the next chunk (8 F floats per lane); the
+    // draw sums need a few more
+    static constexpr int probs = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
+    static constexpr int waves_per_eu = MODE == kFusedProbs ? probs : (F == 4 ? 5 : (F == 8 ? 3 : probs));
 };
 
 template <int F, bool VEC, int MODE>
-__global__ __launch_bounds__(NT, (FusedOcc<F>::waves_per_eu)) void ts_fused(SoftmaxArgs a) {
+__global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fused(SoftmaxArgs a) {
     static_assert(MODE != kFusedProbsSums || F % 4 == 0, "draw sums need whole 4096-column groups");
     __shared__ float red[NW];
-    __shared__ float gsum[MODE == kFusedProbsSums ? (F >= 4 ? F / 4 : 1) : 1][NW];
     __shared__ float chunk_scale;
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
@@ -217,17 +218,11 @@ __global__ __launch_bounds__(NT, (FusedOcc<F>::waves_per_eu)) void ts_fused(Soft
 #pragma unroll
             for (int d = 0; d < NG; ++d) {
                 const int64_t G = c * NG + d;
-                float h = 0.0f;
-                if (G < a.ngroups) h = prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup);
-                const float ws = wave_reduce<SumOp>(h);
-                if (ln == 0) gsum[d][wv] = ws;
-            }
-            __syncthreads();
-            if (lane < NG && c * NG + lane < a.ngroups) {
-                float gs = gsum[lane][0];
-#pragma unroll
-                for (int w = 1; w < NW; ++w) gs += gsum[lane][w];
-                a.part[row * a.ngroups + c * NG + lane] = make_float2(gs, 0.0f);
+                if (G < a.ngroups) {
+                    const float h = prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup);
+                    const float ws = wave_reduce<SumOp>(h);
+                    if (ln == 0) reinterpret_cast<float*>(a.gpart + row * a.ngroups + G)[wv] = ws;
+                }
             }
         }
 #pragma unroll
@@ -235,7 +230,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F>::waves_per_eu)) void ts_fused(Soft
         mw[0] = nmw[0];
         mw[1] = nmw[1];
         own = next_own;
-        __syncthreads();   // chunk_scale and the group sums are rewritten by the next item
+        __syncthreads();   // chunk_scale is rewritten by the next item
     }
 }
 

@@ -170,12 +170,64 @@ __device__ __forceinline__ void apply_mask_words(int64_t c0, int64_t V, const ui
     }
 }
 
+// Columns at or past V take `fill` (a separate step, so that a prefetch can
+// put it off until the values are used: replacing a value waits for its load).
+template <int NT, int F>
+__device__ __forceinline__ void fill_past_end(int64_t c0, int64_t V, float (&x)[4 * F], float fill) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+        const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (col + e >= V) x[4 * j + e] = fill;
+    }
+}
+
+// Issues the chunk's loads: every one before any value is used, none under a
+// branch (a branch around a load makes the compiler wait for it at the join).
+// Addresses are the chunk's start (uniform) plus a 32-bit lane offset; a lane
+// past V reads the chunk's first column instead, which always exists, and
+// holds garbage until fill_past_end replaces it.
+template <int NT, int F, bool VEC, bool NT_LOAD>
+__device__ __forceinline__ void issue_chunk_loads(const float* __restrict__ row, int64_t c0, int64_t V,
+                                                  float (&x)[4 * F]) {
+    const int t = threadIdx.x;
+    const float* __restrict__ base = row + c0;
+    const int64_t left = V - c0;   // columns from the chunk's start to the row's end (> 0)
+    if constexpr (VEC) {
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const uint32_t off = static_cast<uint32_t>((j * NT + t) * 4);
+            const f4* p = reinterpret_cast<const f4*>(base + (off < left ? off : 0u));
+            f4 v;
+            if constexpr (NT_LOAD) v = __builtin_nontemporal_load(p);
+            else v = *p;
+            x[4 * j + 0] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t off = static_cast<uint32_t>((j * NT + t) * 4 + e);
+                const float* p = base + (off < left ? off : 0u);
+                if constexpr (NT_LOAD) x[4 * j + e] = __builtin_nontemporal_load(p);
+                else x[4 * j + e] = *p;
+            }
+        }
+    }
+}
+
+// A whole chunk, ready to use: loads, `fill` past V, and the allowed-id mask
+// (mrow, or none). Every load is issued before any value is used; each sits
+// under its own bounds test, which suits kernels that load the next chunk
+// while working on this one (issue_chunk_loads suits one-shot kernels).
 template <int NT, int F, bool VEC, bool NT_LOAD>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t c0, int64_t V,
                                            float (&x)[4 * F], float fill = kNegInf,
                                            const uint32_t* __restrict__ mrow = nullptr) {
     const int t = threadIdx.x;
-    // every load is issued before any value is used
     if constexpr (VEC) {
 #pragma unroll
         for (int j = 0; j < F; ++j) {

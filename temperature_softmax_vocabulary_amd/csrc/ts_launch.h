@@ -41,8 +41,9 @@ struct SoftmaxArgs {
     int64_t V;
     int64_t nch;           // chunks per row (split, fused)
     int64_t items;         // B * nch
-    float2* part;          // split: [B * nch] chunk partials (pm, pl); fused with
-                           // draw sums: [B * ngroups] (sum of probs, 0) per group
+    float2* part;          // split: [B * nch] chunk partials (pm, pl)
+    float4* gpart;         // fused with draw sums: [B * ngroups] per group, the sums of
+                           // its probabilities held by each of the 4 waves
     float2* bpart;         // fused with draw sums: [B * ngroups * 64] (sum of probs, 0) per block
     int64_t ngroups;       // groups of kDrawGroup columns per row (fused with draw sums)
     unsigned long long* slots;   // [B * kSlotStride] tagged (pm, pl) slots of the fused kernel
@@ -70,8 +71,9 @@ struct DrawArgs {
     int64_t mwords;
     const float* uniforms;    // [B, K]
     int32_t* out_ids;         // [B, K]
-    float2* gpart;            // [B, ngroups] group partials: (max, sum exp2) or (positive sum, 0)
-    float2* bpart;            // [B, ngroups, 64] block partials, same pairs
+    float4* gpart;            // [B, ngroups] group partials: (max, sum exp2, 0, 0) from logits,
+                              // or the positive sums held by each of the 4 waves
+    float2* bpart;            // [B, ngroups, 64] block partials: (max, sum exp2) or (positive sum, 0)
     int64_t B;
     int64_t V;
     int64_t K;

@@ -65,6 +65,10 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
     return v;
 }
 
+// A group's weight from its probability partials: the four waves' sums, added
+// in one fixed order.
+__device__ __forceinline__ float group_prob_sum(float4 v) { return (v.x + v.y) + (v.z + v.w); }
+
 // Block sums of probabilities for one group of a chunk held in the layout of
 // load_chunk with 256 lanes: the group is the four 1024-column chunk groups
 // j0 .. j0 + 3, and block b = 16 (j - j0) + t / 16 is the 4 entries of each of

@@ -160,16 +160,19 @@ ts_status resident_cap(int kind, int F, bool vec, int64_t* cap) {
     return TS_OK;
 }
 
-// The work-split table, from graph-replayed timings on MI355X of every
-// variant and chunk size over B in {1, 3, 8, 16, 64}, V in {151936, 201088,
-// 262144}:
+// The work-split table, from cold timings on MI355X of every variant and
+// chunk size over B in {1, 3, 8, 16, 32, 64, 128, 256} and V in {151936,
+// 201088, 262144}:
 //  - a row that fits one workgroup's registers: one workgroup per row (single
 //    read, no partials);
-//  - B*V <= 2^21 elements: fused, 4096-column chunks (more, smaller workgroups
-//    win while the launch is latency-bound);
-//  - larger: fused, 16384-column chunks (fewest partials; the persistent grid
-//    overlaps waits with the next chunk's loads);
-//  - rows with more than kSlotStride chunks even at 16384 columns: split pair.
+//  - B*V <= 2^21 elements: fused, 4096-column chunks (the launch is
+//    latency-bound; more, smaller workgroups);
+//  - larger: fused, 8192-column chunks (four workgroups per CU hide the waits
+//    better than two of 16384 columns, and a short last chunk wastes less:
+//    at B=64 it is 22.7 against 23.2 us for V=262144 and 14.7 against 17.6 us
+//    for V=151936);
+//  - rows of more than kSlotStride such chunks: fused at 16384 columns while
+//    that fits, else the split pair.
 ts_status choose_plan(int64_t B, int64_t V, bool vec, Plan* p) {
     (void)vec;
     if (V <= tsk::kRowwiseResidentMaxV) {
@@ -178,6 +181,10 @@ ts_status choose_plan(int64_t B, int64_t V, bool vec, Plan* p) {
     }
     if (B * V <= (int64_t(1) << 21) && cdiv(V, 4096) <= tsk::kSlotStride) {
         *p = Plan{TS_VARIANT_FUSED, 4};
+        return TS_OK;
+    }
+    if (cdiv(V, 8192) <= tsk::kSlotStride) {
+        *p = Plan{TS_VARIANT_FUSED, 8};
         return TS_OK;
     }
     if (cdiv(V, 16384) <= tsk::kSlotStride) {
@@ -288,13 +295,22 @@ ts_status launch_softmax(SoftmaxCall& call, const WsView& v, bool group_sums, bo
     a.err = v.err;
     if (call.plan.variant == TS_VARIANT_FUSED) {
         int mode = tsk::kFusedProbs;
+        int64_t grid = call.grid;
         if (group_sums && call.plan.F % 4 == 0) {   // chunks of whole draw groups
-            mode = tsk::kFusedProbsSums;
-            a.ngroups = cdiv(a.V, tsk::kDrawGroup);
-            a.bpart = v.part + a.B * a.ngroups;
-            *sums = true;
+            // this mode has its own occupancy: the grid must fit it too
+            int64_t cap = 0;
+            ts_status st = resident_cap(tsk::kFusedProbsSums, call.plan.F, call.vec, &cap);
+            if (st != TS_OK) return st;
+            if (a.nch <= cap) {
+                mode = tsk::kFusedProbsSums;
+                grid = fused_grid(a.items, a.nch, cap);
+                a.ngroups = cdiv(a.V, tsk::kDrawGroup);
+                a.gpart = reinterpret_cast<float4*>(v.part);
+                a.bpart = v.part + 2 * a.B * a.ngroups;
+                *sums = true;
+            }
         }
-        return hip_status(tsk::launch_fused(a, call.plan.F, call.vec, mode, call.grid, stream));
+        return hip_status(tsk::launch_fused(a, call.plan.F, call.vec, mode, grid, stream));
     }
     return hip_status(tsk::launch_split(a, call.plan.F, call.vec, stream));
 }
@@ -314,9 +330,9 @@ ts_status run_softmax(const float* logits, const float* temps, const uint32_t* a
     return launch_softmax(call, ws_view(*w), false, nullptr, stream);
 }
 
-// Workspace partials of a draw: per row, one per group of 4096 columns, then
-// 64 per group (its blocks of 64 columns).
-int64_t draw_parts(int64_t B, int64_t V) { return B * cdiv(V, tsk::kDrawGroup) * (1 + tsk::kBlocksPerGroup); }
+// Workspace partials of a draw, in float2 units: per row, one float4 per group
+// of 4096 columns, then 64 float2 per group (its blocks of 64 columns).
+int64_t draw_parts(int64_t B, int64_t V) { return B * cdiv(V, tsk::kDrawGroup) * (2 + tsk::kBlocksPerGroup); }
 
 // The draw's two kernels (draw_kernels.hip) on x = logits (kDrawLogits) or
 // probabilities (kDrawProbs); partials_done: the partials are already in the
@@ -335,8 +351,8 @@ ts_status launch_draw(int kind, const float* x, const float* temps, const uint32
     d.V = V;
     d.K = K;
     d.ngroups = cdiv(V, tsk::kDrawGroup);
-    d.gpart = v.part;
-    d.bpart = v.part + B * d.ngroups;
+    d.gpart = reinterpret_cast<float4*>(v.part);
+    d.bpart = v.part + 2 * B * d.ngroups;
     const bool vec = aligned16(x) && (V % 4 == 0);
     if (!partials_done) {
         hipError_t e = tsk::launch_draw_partials(d, vec, kind, stream);
