@@ -7,8 +7,9 @@ A step is one ts_softmax call over one batch: B=64 rows of V=262144 float32
 logits (N(0,1)*4, temperatures U[0.5, 1.5), one quarter of the rows each
 unmasked / first 16384 columns -inf / a random 20000-column -inf block / all
 but 3 ids -inf). Inputs are resident in HBM before timing. Calls rotate over
-enough buffer sets (>= 512 MiB of logits + probs) that each call finds its
-logits outside the 256 MiB Infinity Cache: the headline is this cold rate.
+enough buffer sets (>= 1 GiB of logits + probs, 512 MiB of logits alone) that
+each call finds its logits outside the 256 MiB Infinity Cache: the headline
+is this cold rate.
 
 Prints one JSON line. `value` is the algorithmic HBM rate 2*B*V*4 bytes per
 call over the timed region (GB/s); `roofline` compares the per-launch rate of
@@ -42,7 +43,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "µs/call and HBM GB/s (% of peak) for B×V fp32 temperature softmax"
 DEFAULT_WORKLOAD = "B64_V262144_masked_quarters"
-COLD_FOOTPRINT = 512 << 20     # >= 2x the 256 MiB Infinity Cache
+COLD_FOOTPRINT = 1 << 30   # bytes of logits + probs the timed calls rotate over: 4x the 256 MiB Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "temperature_softmax_vocabulary_amd", "csrc")
 
