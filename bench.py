@@ -179,6 +179,42 @@ def _elapsed_us(torch, fn, n):
     return e0.elapsed_time(e1) * 1000.0 / n
 
 
+def configs_graph_us(torch, tsv, workloads, dev) -> dict:
+    """µs per ts_softmax call for each of the five workloads, cold, from graph
+    replay (launch gaps removed): rotating slices of one >= 512 MiB buffer
+    pair, all captured into one graph."""
+    res = {}
+    for name in workloads.CONFIG_ORDER:
+        w = workloads.make_config(name)
+        B, V = w.B, w.V
+        nsets = min(512, max(2, math.ceil((512 << 20) / (2 * B * V * 4))))
+        x = torch.from_numpy(w.logits).to(dev).unsqueeze(0).repeat(nsets, 1, 1)
+        t = torch.from_numpy(w.temps).to(dev)
+        y = torch.empty_like(x)
+        s = torch.cuda.Stream(device=dev)
+        tsv.ts_reserve(B, V, device=dev, stream=s)
+        with torch.cuda.stream(s):
+            for i in range(nsets):
+                tsv.ts_softmax(x[i], t, out=y[i])
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(nsets):
+                tsv.ts_softmax(x[i], t, out=y[i])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1000.0 / (reps * nsets), 3)
+        del x, y, g
+    return res
+
+
 def cpu_baseline(w, target_s: float):
     """The float64 oracle, as it stands, on the host over the same workload."""
     from oracle import softmax_ref
@@ -378,6 +414,8 @@ def main(argv=None) -> int:
             masked(i)
         extras["masked_bitmask_us_per_call"] = round(_elapsed_us(torch, masked, 200), 3)
         del xms, bitss
+        # every workload, graph replay (the small ones are launch-bound)
+        extras["configs_graph_us_per_call"] = configs_graph_us(torch, tsv, workloads, dev)
         dp = torch.cuda.get_device_properties(dev)
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
                             "gcn_arch": getattr(dp, "gcnArchName", "")}

@@ -175,8 +175,8 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  *                 same integer prefix sums over groups of 1024 ids; every id
  *                 drawn has a finite logit (and an allowed bit); -1 for a row
  *                 with none. With probs_out the draw reads the written
- *                 probabilities (the ids equal ts_sample's on them); without,
- *                 it works from the logits (one read of them in all).
+ *                 probabilities; without, it works from the logits (one read
+ *                 of them in all).
  * Errors        : as ts_softmax and ts_sample. K == 0 reduces to ts_softmax
  *                 (or a no-op when probs_out is NULL).
  */

@@ -22,7 +22,6 @@
 #include "ts_device.h"
 #include "ts_exchange.h"
 #include "ts_launch.h"
-#include "ts_sample_device.h"
 
 namespace tsk {
 
@@ -115,15 +114,18 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 // launches no more workgroups than the device holds at once and at least nch.
 //
 // MODE kFusedProbs writes the probabilities; kFusedProbsSums also writes the
-// sums of the probabilities per group of 4096 columns and per block of 64, for
-// a token draw that follows (draw_kernels.hip).
+// sums of the probabilities per group of 4096 columns (one share per wave) and
+// per block of 64, for a token draw that follows (draw_kernels.hip). They are
+// formed from the exponentials while the kernel waits on its row, then
+// multiplied by the chunk's scale: within float rounding of the sums of the
+// written probabilities.
 // ---------------------------------------------------------------------------
 template <int F, int MODE>
 struct FusedOcc {
     // registers hold the current and the next chunk (8 F floats per lane); the
     // draw sums need a few more
     static constexpr int probs = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
-    static constexpr int waves_per_eu = MODE == kFusedProbs ? probs : (F == 4 ? 5 : (F == 8 ? 3 : probs));
+    static constexpr int waves_per_eu = probs;
 };
 
 template <int F, bool VEC, int MODE>
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
     static_assert(MODE != kFusedProbsSums || F % 4 == 0, "draw sums need whole 4096-column groups");
     __shared__ float red[NW];
     __shared__ float chunk_scale;
+    __shared__ float bsum[MODE == kFusedProbsSums ? F : 1][16];   // draw sums: per block of a chunk
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
     int64_t item = blockIdx.x;
@@ -185,6 +188,17 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
             if (lane == 0) next_own = slot_load(a.slots + nr * kSlotStride + nc);
         }
 
+        // draw sums: block sums of the exponentials, formed while the row's
+        // other chunks arrive and parked in LDS; after the wait they are scaled
+        // to probabilities and written (with each wave's share of each group)
+        if constexpr (MODE == kFusedProbsSums) {
+#pragma unroll
+            for (int j = 0; j < F; ++j) {
+                const float b = row16_reduce<SumOp>((x[4 * j] + x[4 * j + 1]) + (x[4 * j + 2] + x[4 * j + 3]));
+                if ((lane & 15) == 15) bsum[j][lane >> 4] = b;
+            }
+        }
+
         // wave 0 waits for the row's partials and combines them: gm = max pm,
         // gl = sum pl exp2((pm - gm) k), a fully masked chunk adding exactly 0
         if (lane < kWave) {
@@ -211,17 +225,27 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
         for (int i = 0; i < 4 * F; ++i) x[i] *= scale;    // the probabilities
         store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
         if constexpr (MODE == kFusedProbsSums) {
-            // the draw's group and block sums of the probabilities just written
-            // (the same sums the draw's partials kernel forms from them)
-            constexpr int NG = F / 4;   // draw groups per chunk
-            const int ln = lane & (kWave - 1), wv = lane / kWave;
-#pragma unroll
-            for (int d = 0; d < NG; ++d) {
+            // bsum is complete: the barrier after the wait follows every write.
+            // Lane t < 16 F writes block (t / 16, t % 16); a group's share of
+            // wave w is the sum of its blocks in that wave's 4 rows of lanes.
+            constexpr int NG = F / 4;
+            if (lane < 16 * F) {
+                const int j = lane >> 4, r = lane & 15;
+                const int64_t G = c * NG + j / 4;
+                if (G < a.ngroups)
+                    a.bpart[(row * a.ngroups + G) * kBlocksPerGroup + (j % 4) * 16 + r] =
+                        make_float2(bsum[j][r] * scale, 0.0f);
+            }
+            if (lane < NG * NW) {
+                const int d = lane / NW, w = lane % NW;
                 const int64_t G = c * NG + d;
                 if (G < a.ngroups) {
-                    const float h = prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup);
-                    const float ws = wave_reduce<SumOp>(h);
-                    if (ln == 0) reinterpret_cast<float*>(a.gpart + row * a.ngroups + G)[wv] = ws;
+                    float h = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        h += (bsum[4 * d + jj][4 * w] + bsum[4 * d + jj][4 * w + 1]) +
+                             (bsum[4 * d + jj][4 * w + 2] + bsum[4 * d + jj][4 * w + 3]);
+                    reinterpret_cast<float*>(a.gpart + row * a.ngroups + G)[w] = h * scale;
                 }
             }
         }
@@ -230,7 +254,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
         mw[0] = nmw[0];
         mw[1] = nmw[1];
         own = next_own;
-        __syncthreads();   // chunk_scale is rewritten by the next item
+        __syncthreads();   // chunk_scale (and the draw sums) are rewritten by the next item
     }
 }
 
