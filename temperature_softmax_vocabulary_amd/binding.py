@@ -207,11 +207,11 @@ def ts_sample(probs: torch.Tensor, uniforms: torch.Tensor, out_ids: Optional[tor
 def ts_softmax_sample(logits: torch.Tensor, temps: torch.Tensor, uniforms: torch.Tensor,
                       out_ids: Optional[torch.Tensor] = None, probs_out=False,
                       stream=None, allowed: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Softmax and inverse-CDF draw in one pass over the logits.
+    """Softmax and inverse-CDF draw in one call.
 
     Returns (ids [B, K] int32, probs [B, V] or None). probs_out: False (do not
-    write the probabilities), True (allocate them) or a [B, V] float32 tensor
-    (may be `logits` itself)."""
+    write the probabilities: the draw works from the logits), True (allocate
+    them) or a [B, V] float32 tensor (may be `logits` itself)."""
     B, V, _ = _softmax_args(logits, temps, logits)
     _need(uniforms, "uniforms", torch.float32, 2)
     if uniforms.shape[0] != B or uniforms.device != logits.device:
