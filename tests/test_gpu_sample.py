@@ -125,3 +125,45 @@ def test_unnormalised_weights_scale_by_total():
     u = rng.random((4, 256)).astype(np.float32)
     ids = _sample(p, u)
     assert_ids_valid(ids, p, u)
+
+
+def test_dyadic_rows_exact_across_groups_and_blocks():
+    # Weights 2^-e spread over several 4096-id groups and 64-id blocks (some
+    # blocks and groups empty): every float sum is exact, so every level of the
+    # draw is exact and the ids must equal the oracle's, at and next to every
+    # CDF boundary.
+    V = 3 * 4096 + 100
+    rng = np.random.default_rng(21)
+    B = 4
+    p = np.zeros((B, V), np.float32)
+    for r in range(B):
+        ids = np.sort(rng.choice(V, size=16, replace=False))
+        p[r, ids] = np.float32(2.0) ** -rng.integers(1, 6, size=16).astype(np.float32)
+    p[0, :] = 0
+    p[0, [5, 4096 + 64, 2 * 4096 + 63, V - 1]] = [0.5, 0.25, 0.125, 0.125]   # one id per group, block edges
+    c = np.cumsum(p.astype(np.float64), axis=1)
+    us = []
+    for r in range(B):
+        t = c[r, -1]
+        cuts = np.unique(c[r]) / t
+        row = np.concatenate([cuts, np.nextafter(cuts.astype(np.float32), np.float32(0)),
+                              np.nextafter(cuts.astype(np.float32), np.float32(2)), [0.0, 1.0]])
+        us.append(np.resize(row, 64))
+    u = np.array(us, np.float32)
+    ids = _sample(p, u)
+    np.testing.assert_array_equal(ids, sample_ref(p, u))
+
+
+def test_nan_and_negative_entries_are_never_drawn():
+    # entries that are not > 0 hold no mass: they are skipped whatever the
+    # uniform, and they do not poison the rest of the row
+    rng = np.random.default_rng(22)
+    V = 9000
+    p = rng.random((3, V)).astype(np.float32)
+    bad = rng.random((3, V)) < 0.3
+    p[bad] = np.where(rng.random(int(bad.sum())) < 0.5, np.float32(np.nan), np.float32(-1.0))
+    u = rng.random((3, 512)).astype(np.float32)
+    ids = _sample(p, u)
+    clean = np.where(p > 0, p, 0).astype(np.float32)
+    assert_ids_valid(ids, clean, u, what="nan/negative")
+    assert not bad[np.arange(3)[:, None], ids].any()

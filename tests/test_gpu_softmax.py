@@ -174,3 +174,17 @@ def test_plan_for_configs_is_legal():
         v, ch = tsv.ts_plan(c["B"], c["V"])
         assert v in (tsv.TS_VARIANT_FUSED, tsv.TS_VARIANT_SPLIT, tsv.TS_VARIANT_ROWWISE)
         assert v == tsv.TS_VARIANT_ROWWISE or ch in tsv.CHUNKS
+
+
+@pytest.mark.parametrize("V", [2 * 1024 * 1024 + 4099, 4 * 1024 * 1024 + 1000])
+def test_long_rows_default_plan(V):
+    # rows beyond 256 chunks of 8192 (fused at 16384) and of 16384 columns
+    # (the split pair): the plan's upper branches, with masks at chunk starts
+    w = workloads.make(2, V, "block_and_head")
+    ref = softmax_ref(w.logits, w.temps)
+    plan = tsv.ts_plan(2, V)
+    print(f"[gpu] long rows V={V} plan={plan}", flush=True)
+    y = tsv.ts_softmax(torch.from_numpy(w.logits).to(DEV), torch.from_numpy(w.temps).to(DEV)).cpu().numpy()
+    assert_softmax_matches(y, w.logits, w.temps, ref, what=f"V={V}")
+    expect = tsv.TS_VARIANT_FUSED if V <= 256 * 16384 else tsv.TS_VARIANT_SPLIT
+    assert plan[0] == expect
