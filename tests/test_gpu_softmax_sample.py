@@ -65,14 +65,15 @@ def test_matches_separate_softmax_then_sample():
     probs_s = tsv.ts_softmax(x, t)
     ids_s = tsv.ts_sample(probs_s, u)
     torch.cuda.synchronize()
-    # the same work split: the probabilities are bitwise the same; the ids can
-    # differ only where a target sits within float rounding of a block or group
-    # boundary (the fused kernel sums before scaling, ts_sample after)
-    assert torch.equal(probs_f, probs_s)
-    ref = softmax_ref(w.logits, w.temps).astype(np.float32)
+    # both paths meet the oracle's gates; the probabilities agree to float
+    # rounding (the work split may differ), and the ids can differ only where a
+    # target sits within rounding of a block or group boundary
+    ref = softmax_ref(w.logits, w.temps)
+    assert_softmax_matches(probs_f.cpu().numpy(), w.logits, w.temps, ref, what="fused with draw")
+    assert_softmax_matches(probs_s.cpu().numpy(), w.logits, w.temps, ref, what="separate")
     a, b = ids_f.cpu().numpy(), ids_s.cpu().numpy()
-    assert_ids_valid(a, ref, w.uniforms, what="fused")
-    assert_ids_valid(b, ref, w.uniforms, what="separate")
+    assert_ids_valid(a, ref.astype(np.float32), w.uniforms, what="fused")
+    assert_ids_valid(b, ref.astype(np.float32), w.uniforms, what="separate")
     assert np.mean(a == b) > 0.99
 
 
