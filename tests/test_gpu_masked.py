@@ -110,3 +110,18 @@ def test_softmax_sample_with_mask_draws_only_allowed_ids():
     assert_ids_valid(ids, ref.astype(np.float32), w.uniforms, what="masked draw")
     keep = np.isfinite(w.logits)
     assert np.all(keep[np.arange(w.B)[:, None], ids])
+
+
+def test_ids_only_draw_with_mask_draws_only_allowed_ids():
+    # the draw straight from the logits applies the bits in both of its kernels
+    # (group and block partials, then the chosen block's entries)
+    for name in ("B3_V151936_pr_test_rows", "B64_V262144_masked_quarters"):
+        w, x, bits = _case(name)
+        ref = softmax_ref(w.logits, w.temps)
+        ids, none = tsv.ts_softmax_sample(torch.from_numpy(x).to(DEV), torch.from_numpy(w.temps).to(DEV),
+                                          torch.from_numpy(w.uniforms).to(DEV), allowed=_bits(bits))
+        torch.cuda.synchronize()
+        assert none is None
+        ids = ids.cpu().numpy()
+        assert_ids_valid(ids, ref.astype(np.float32), w.uniforms, what=f"{name} ids only, masked")
+        assert np.all(np.isfinite(w.logits)[np.arange(w.B)[:, None], ids])
