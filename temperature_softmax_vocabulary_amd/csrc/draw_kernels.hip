@@ -10,16 +10,16 @@
 // A row is cut into groups of 4096 columns, each of 64 blocks of 64 columns,
 // and the draw takes two short kernels:
 //  ts_draw_partials: one read of the row, no exchange between workgroups. Each
-//    group and each block gets a float partial: from logits, the method's
-//    chunk partial (pm, pl) -- the max, and the sum of exp2((x - shift) k) with
-//    the -inf guard of the fix paragraph, at the block's own max (a group's pl
-//    combines its blocks' as the finalize combines chunks); from
-//    probabilities, the sum of the positive entries.
+//    group gets a float partial: from logits, the method's chunk partial
+//    (pm, pl) -- the group's max and the sum of exp2((x - shift) k) with the
+//    -inf guard of the fix paragraph; from probabilities, the sum of the
+//    positive entries (one share per wave). Each block gets its sum of the
+//    same terms: the exponentials at its group's max, or the probabilities.
 //  ts_draw_resolve: one wave per (row, target), three levels. At each level
-//    the 64 lanes hold 64 float weights -- the row's groups, then the chosen
-//    group's blocks, then the chosen block's entries (for logits, rescaled to
-//    the level's max as in the finalize, so that a fully masked group or block
-//    weighs exactly 0) -- which become integers at one power-of-two scale; an
+//    the 64 lanes hold 64 float weights -- the row's groups (for logits, their
+//    pl rescaled to the row's max as in the finalize, so that a fully masked
+//    group weighs exactly 0), then the chosen group's blocks, then the chosen
+//    block's entries -- which become integers at one power-of-two scale; an
 //    integer prefix sum over the lanes gives each its range, and the lane whose
 //    range holds the target is chosen. The target is carried into the next
 //    level's integer units in double precision and clamped to its total.
@@ -96,45 +96,31 @@ __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
             if (mrow) apply_mask_words<DT, F>(c0, a.V, mw, x);
         }
         const float k = exp2_scale(a.temps[row]);
-        float bm[F], bl[F];
+        // each group's max over the workgroup; then its exponentials at that max,
+        // summed per block and per group as probabilities are
+        float gm[GPW];
 #pragma unroll
-        for (int j = 0; j < F; ++j) {
-            bm[j] = row16_reduce<MaxOp>(fmaxf(fmaxf(x[4 * j], x[4 * j + 1]), fmaxf(x[4 * j + 2], x[4 * j + 3])));
-            const float sh = guarded_shift(bm[j]);
-            float l[4];
+        for (int d = 0; d < GPW; ++d) {
+            float m = kNegInf;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) l[e] = exp2_hw((x[4 * j + e] - sh) * k);
-            bl[j] = row16_reduce<SumOp>((l[0] + l[1]) + (l[2] + l[3]));
+            for (int i = 16 * d; i < 16 * d + 16; ++i) m = fmaxf(m, x[i]);
+            gm[d] = m;
         }
-        // each group: max of its block maxima, and its blocks' sums rescaled to it
-        float gm[GPW], gl[GPW];
-#pragma unroll
-        for (int d = 0; d < GPW; ++d)
-            gm[d] = fmaxf(fmaxf(bm[4 * d], bm[4 * d + 1]), fmaxf(bm[4 * d + 2], bm[4 * d + 3]));
         block_reduce_n<MaxOp, DW, GPW>(gm, red);
+        float gl[GPW];
 #pragma unroll
         for (int d = 0; d < GPW; ++d) {
             const float gsh = guarded_shift(gm[d]);
-            gl[d] = 0.0f;
-            if (holder)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int j = 4 * d + jj;
-                    gl[d] += masked_term(bm[j], bl[j] * exp2_hw((bm[j] - gsh) * k));
-                }
+            for (int i = 16 * d; i < 16 * d + 16; ++i) x[i] = exp2_hw((x[i] - gsh) * k);
+            const int64_t G = G0 + d;   // (workgroup-uniform test: a group past the row's end writes nothing)
+            gl[d] = G < a.ngroups ? prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup)
+                                  : 0.0f;
         }
         block_reduce_n<SumOp, DW, GPW>(gl, red);
 #pragma unroll
-        for (int d = 0; d < GPW; ++d) {
-            const int64_t G = G0 + d;
-            if (G >= a.ngroups) break;
-            if (holder) {
-                float2* bgroup = a.bpart + (row * a.ngroups + G) * kBlocksPerGroup;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) bgroup[jj * 16 + (t >> 4)] = make_float2(bm[4 * d + jj], bl[4 * d + jj]);
-            }
-            if (t == 0) a.gpart[row * a.ngroups + G] = make_float4(gm[d], gl[d], 0.0f, 0.0f);
-        }
+        for (int d = 0; d < GPW; ++d)
+            if (t == 0 && G0 + d < a.ngroups) a.gpart[row * a.ngroups + G0 + d] = make_float4(gm[d], gl[d], 0.0f, 0.0f);
     } else {
         issue_chunk_loads<DT, F, VEC, true>(a.x + row * a.V, G0 * kDrawGroup, a.V, x);
         fill_past_end<DT, F>(G0 * kDrawGroup, a.V, x, 0.0f);
@@ -247,15 +233,8 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     }
 
     // level 2: the group's 64 blocks, lane l holding block l
-    const float2 bv = a.bpart[(row * ng + G) * kBlocksPerGroup + ln];
-    float bw;
-    if constexpr (KIND == kDrawLogits) {
-        // rescaled to the group's max (every block max is <= it)
-        const float bsh = guarded_shift(grow[G].x);
-        bw = masked_term(bv.x, bv.y * exp2_hw((bv.x - bsh) * k));
-    } else {
-        bw = bv.x;
-    }
+    // (block weights: sums of the group's exponentials at its max, or of probabilities)
+    const float bw = a.bpart[(row * ng + G) * kBlocksPerGroup + ln].x;
     const int s2 = scale_exponent(wave_reduce<SumOp>(bw));   // > 0: qG >= 1 needs a positive group
     const uint64_t qb = fixed_point(bw, s2);
     const uint64_t incl2 = wave_inclusive_scan_u64(qb);
@@ -267,22 +246,19 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     }
     const uint64_t Pb = lane_value_u64(incl2 - qb, b);
     const uint64_t qbb = lane_value_u64(qb, b);
-    const float bx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv.x), b));
+    const float bx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bw), b));   // > 0
 
     // level 3: the block's 64 entries, lane l holding column G 4096 + 64 b + l
     const int64_t col = G * kDrawGroup + static_cast<int64_t>(b) * kDrawBlock + ln;
     const float* xr = a.x + row * a.V;
     float v = col < a.V ? xr[col] : (KIND == kDrawLogits ? kNegInf : 0.0f);
-    int s3;
     if constexpr (KIND == kDrawLogits) {
         if (const uint32_t* mrow = draw_mask_row(a, row)) {
             if (col < a.V && !((mrow[col >> 5] >> (col & 31)) & 1u)) v = kNegInf;
         }
-        v = exp2_hw((v - guarded_shift(bx)) * k);   // <= 1 at the block's max
-        s3 = 61 - 6;                                 // 64 entries <= 1: total <= 2^61
-    } else {
-        s3 = scale_exponent(bx);                     // > 0: the block was chosen
+        v = exp2_hw((v - guarded_shift(grow[G].x)) * k);   // as the partials kernel formed them
     }
+    const int s3 = scale_exponent(bx);   // each entry <= the block's sum
     const uint64_t qe = fixed_point(v, s3);
     const uint64_t incl3 = wave_inclusive_scan_u64(qe);
     const uint64_t T3 = carry_target(T2, Pb, qbb, lane_value_u64(incl3, kWave - 1));

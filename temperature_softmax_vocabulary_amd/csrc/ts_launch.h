@@ -73,7 +73,8 @@ struct DrawArgs {
     int32_t* out_ids;         // [B, K]
     float4* gpart;            // [B, ngroups] group partials: (max, sum exp2, 0, 0) from logits,
                               // or the positive sums held by each of the 4 waves
-    float2* bpart;            // [B, ngroups, 64] block partials: (max, sum exp2) or (positive sum, 0)
+    float2* bpart;            // [B, ngroups, 64] block partials: (sum, 0) of the exponentials at the
+                              // group's max, or of the positive probabilities
     int64_t B;
     int64_t V;
     int64_t K;
