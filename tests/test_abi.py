@@ -123,3 +123,20 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
         text = open(path).read()
         assert "oracle" not in text.replace("oracle's", ""), path
         assert "torch.softmax" not in text and "np.exp" not in text, path
+
+
+@pytest.mark.parametrize("B,V,expect", [
+    (1, 16384, (binding.TS_VARIANT_ROWWISE, 0)),            # the row fits one workgroup's registers
+    (64, 5003, (binding.TS_VARIANT_ROWWISE, 0)),
+    (1, 151936, (binding.TS_VARIANT_FUSED, 4096)),           # B*V <= 2^21: latency-bound, small chunks
+    (8, 262144, (binding.TS_VARIANT_FUSED, 4096)),           # exactly 2^21
+    (16, 201088, (binding.TS_VARIANT_FUSED, 8192)),
+    (64, 262144, (binding.TS_VARIANT_FUSED, 8192)),          # the bench workload
+    (2, 2 * 1024 * 1024 + 4099, (binding.TS_VARIANT_FUSED, 16384)),   # > 256 chunks of 8192
+    (2, 4 * 1024 * 1024 + 1000, (binding.TS_VARIANT_SPLIT, 16384)),   # > 256 chunks of 16384
+])
+def test_work_split_table(L, B, V, expect):
+    # the measured table of the work split (host only, no device needed)
+    v, c = ctypes.c_int32(), ctypes.c_int32()
+    assert L.ts_plan(B, V, ctypes.byref(v), ctypes.byref(c)) == binding.TS_OK
+    assert (v.value, c.value) == expect
