@@ -104,10 +104,14 @@ def _per_dispatch(rows, counter: str, name_part: str):
 
 
 def summarize_counters(fetch_dir: str, write_dir: str, workload: str, kernel_name: str, kernel_tag: str,
-                       command: str) -> str:
+                       command: str, alg_bytes=None) -> str:
+    """Per-dispatch HBM bytes of one kernel from two rocprofv3 --pmc runs, scaled
+    by the copy kernel's counters; alg_bytes: the kernel's algorithmic bytes per
+    launch (default: the softmax's 2 B V 4)."""
     from temperature_softmax_vocabulary_amd import workloads
     c = workloads.CONFIGS[workload]
     n_bytes = c["B"] * c["V"] * 4
+    alg = 2 * n_bytes if alg_bytes is None else int(alg_bytes)
     fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
     f_k, nf = _per_dispatch(fr, "FETCH_SIZE", kernel_name)
     w_k, nw = _per_dispatch(wr, "WRITE_SIZE", kernel_name)
@@ -135,8 +139,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, kernel_nam
         f.write(f"fetch_factor={ff:.4f}\nwrite_factor={wf:.4f}\n")
         f.write(f"fetch_bytes_per_launch={fetch_b:.0f}\nwrite_bytes_per_launch={write_b:.0f}\n")
         f.write(f"traffic_bytes_per_launch={fetch_b + write_b:.0f}\n")
-        f.write(f"algorithmic_bytes_per_launch={2 * n_bytes}\n")
-        f.write(f"traffic_over_algorithmic={(fetch_b + write_b) / (2 * n_bytes):.4f}\n")
+        f.write(f"algorithmic_bytes_per_launch={alg}\n")
+        f.write(f"traffic_over_algorithmic={(fetch_b + write_b) / alg:.4f}\n")
     return out
 
 
@@ -251,7 +255,11 @@ def main(argv=None) -> int:
     ap.add_argument("--profile-command", default="python3 bench.py --steps 200 --warmup 20 --no-cpu-baseline",
                     help="the profiled command, recorded in the summaries")
     ap.add_argument("--summary-tag", default=None,
-                    help="file tag of a trace summary (default: the profiled kernel's)")
+                    help="file tag of a summary (default: the profiled kernel's)")
+    ap.add_argument("--kernel-name", default=None,
+                    help="summarize this kernel (name substring) instead of the plan's")
+    ap.add_argument("--alg-bytes", type=int, default=None,
+                    help="algorithmic bytes per launch of --kernel-name (counter summaries)")
     args = ap.parse_args(argv)
     if args.no_extras:
         args.extras = "none"
@@ -268,15 +276,18 @@ def main(argv=None) -> int:
 
     if args.summarize_counters or args.summarize_trace:
         # host-side parsing only; the plan is given or read from the trace
-        if not args.variant:
-            raise SystemExit("--summarize-* needs --variant and --chunk of the profiled plan")
-        name, tag = _kernel_names(tsv, (args.variant, args.chunk))
+        if args.kernel_name:
+            name, tag = args.kernel_name, args.summary_tag or "kernel"
+        elif not args.variant:
+            raise SystemExit("--summarize-* needs --variant and --chunk of the profiled plan, or --kernel-name")
+        else:
+            name, tag = _kernel_names(tsv, (args.variant, args.chunk))
         if args.summarize_trace:
             print(summarize_trace(args.summarize_trace, args.workload, name, args.summary_tag or tag,
                                   args.profile_command))
         if args.summarize_counters:
             print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
-                                     name, tag, args.profile_command))
+                                     name, args.summary_tag or tag, args.profile_command, args.alg_bytes))
         return 0
 
     if not torch.cuda.is_available():
