@@ -48,9 +48,27 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "temperature_softmax_vocabulary_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+# The sources each profiled kernel is built and launched from: a summary stays
+# valid until one of them changes.
+KERNEL_SOURCES = {
+    "ts_fused": ["softmax_kernels.hip", "ts_device.h", "ts_exchange.h", "ts_launch.h", "tsoftmax_api.cpp"],
+    "ts_split": ["softmax_kernels.hip", "ts_device.h", "ts_launch.h", "tsoftmax_api.cpp"],
+    "ts_rowwise": ["softmax_kernels.hip", "ts_device.h", "ts_launch.h", "tsoftmax_api.cpp"],
+    "ts_draw": ["draw_kernels.hip", "ts_sample_device.h", "ts_device.h", "ts_launch.h", "tsoftmax_api.cpp"],
+}
+
+
+def kernel_source_hash(kernel_tag: str = "") -> str:
+    """sha256 prefix over the sources of the kernel family `kernel_tag` starts
+    with (every source under csrc/ when it names none of them)."""
+    files = None
+    for family, names in KERNEL_SOURCES.items():
+        if kernel_tag.startswith(family):
+            files = [os.path.join(CSRC, n) for n in names]
+    if files is None:
+        files = glob.glob(os.path.join(CSRC, "*"))
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for p in sorted(files):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -72,7 +90,7 @@ def read_traffic(kernel_tag: str, workload: str):
         if line and not line.startswith("#") and "=" in line:
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(kernel_tag):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -130,7 +148,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, kernel_nam
         f.write(f"# HBM byte counters per dispatch for {kernel_name} on {workload}\n")
         f.write(f"# rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, on: {command}\n")
         f.write("# raw values in KiB per dispatch; scaled by a plain copy of the same bytes\n")
-        f.write(f"kernel_source_sha256={kernel_source_hash()}\n")
+        f.write(f"kernel_source_sha256={kernel_source_hash(kernel_tag)}\n")
         f.write(f"kernel={kernel_name}\n")
         f.write(f"dispatches_fetch={nf}\ndispatches_write={nw}\n")
         f.write(f"fetch_kib={f_k:.1f}\nwrite_kib={w_k:.1f}\n")
@@ -158,7 +176,7 @@ def summarize_trace(trace_dir: str, workload: str, kernel_name: str, kernel_tag:
     with open(out, "w") as f:
         f.write(f"# rocprofv3 kernel trace summary for {workload}; dominant kernel {kernel_name}\n")
         f.write(f"# command: {command}\n")
-        f.write(f"# kernel_source_sha256={kernel_source_hash()}\n")
+        f.write(f"# kernel_source_sha256={kernel_source_hash(kernel_tag)}\n")
         f.write(f"{'kernel':<72} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}\n")
         for r in rows:
             name = r["Name"].replace("(anonymous namespace)::", "")
@@ -431,7 +449,7 @@ def main(argv=None) -> int:
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
                             "gcn_arch": getattr(dp, "gcnArchName", "")}
     if extras:
-        extras["kernel_source_sha256"] = kernel_source_hash()
+        extras["kernel_source_sha256"] = kernel_source_hash(ktag)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:

@@ -143,13 +143,16 @@ ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
  * out_ids  : [B, K] int32. For each (b, k): with C the row's inclusive
  *            prefix sums and target = u * C[V-1], the smallest id j with
  *            C[j] > target; for u = 1 the last id with a positive entry.
- *            Prefix sums are integers: inside each group of 1024 ids, the
- *            entries in 64-bit fixed point at a power-of-two scale (exact);
- *            across groups, the groups' float sums at one power-of-two scale
- *            per row, so a group boundary can sit about 1e-7 of the row total
- *            away from the exact one. The id is always one with a positive
- *            entry. A row with no positive entry (or a sum that is not
- *            finite) gives -1.
+ *            The row is cut into groups of 4096 ids and each group into
+ *            blocks of 64 ids. Prefix sums are integers at three levels: the
+ *            groups' float sums at one power-of-two scale per row, the
+ *            chosen group's block sums at one scale, then the chosen block's
+ *            entries at one scale, each in 64-bit fixed point. Inside a block
+ *            the choice is exact; a group or block boundary can sit about
+ *            1e-7 of the row total away from the exact one (exact when every
+ *            entry is a multiple of one power of two that the sums hold
+ *            exactly). The id is always one with a positive entry. A row
+ *            with no positive entry (or a sum that is not finite) gives -1.
  * Errors   : TS_ERR_INVALID_ARGUMENT for B < 0, K < 0, V < 1,
  *            V > INT32_MAX, a NULL pointer when B*K > 0, or out_ids overlapping
  *            probs or uniforms. B == 0 or K == 0 is a no-op.
@@ -160,8 +163,8 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
 /*
  * The softmax and the token draw in one call: ts_softmax followed by
  * ts_sample. Without probs_out the probabilities are never written: the logits
- * are read once for per-group partials, and only the groups that hold a
- * target are read again. The draw consumes the softmax as in the scope
+ * are read once for per-group and per-block partials, and only the 64-id
+ * blocks that hold a target are read again. The draw consumes the softmax as in the scope
  * paragraph of the pull-request page; every id drawn has a finite logit
  * (results table, sampling row).
  *
@@ -172,7 +175,7 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  *                 probabilities ts_softmax computes (probs_out == logits is
  *                 allowed); if NULL the probabilities are never written.
  * out_ids       : [B, K] int32. The inverse-CDF rule of ts_sample with the
- *                 same integer prefix sums over groups of 1024 ids; every id
+ *                 same three levels of integer prefix sums; every id
  *                 drawn has a finite logit (and an allowed bit); -1 for a row
  *                 with none. With probs_out the draw reads the written
  *                 probabilities; without, it works from the logits (one read
