@@ -122,10 +122,13 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 // ---------------------------------------------------------------------------
 template <int F, int MODE>
 struct FusedOcc {
-    // registers hold the current and the next chunk (8 F floats per lane); the
-    // draw sums need a few more
+    // registers hold the current and the next chunk (8 F floats per lane)
     static constexpr int probs = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
-    static constexpr int waves_per_eu = probs;
+    // the draw sums need a few more: one wave per SIMD less keeps them in
+    // registers at 4096 and 8192 columns (the sums run at 4096 only for small
+    // calls, B V <= 2^21, whose grid is far below the device's capacity either
+    // way, and take 16384 where the plan says 8192)
+    static constexpr int waves_per_eu = MODE != kFusedProbsSums ? probs : (F == 4 ? 5 : (F == 8 ? 3 : probs));
 };
 
 template <int F, bool VEC, int MODE>
@@ -226,26 +229,25 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
         store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
         if constexpr (MODE == kFusedProbsSums) {
             // bsum is complete: the barrier after the wait follows every write.
-            // Lane t < 16 F writes block (t / 16, t % 16); a group's share of
-            // wave w is the sum of its blocks in that wave's 4 rows of lanes.
+            // Block (j, r) of the chunk is block 16 j + r of the row counted from
+            // the chunk's first group, so lane t < 16 F writes block t; lane
+            // t < 4 NG writes wave t % 4's share of group t / 4, the sum of its
+            // blocks in that wave's 4 rows of lanes. (Offsets from a uniform
+            // base: no per-lane 64-bit index is kept across the loop.)
             constexpr int NG = F / 4;
-            if (lane < 16 * F) {
-                const int j = lane >> 4, r = lane & 15;
-                const int64_t G = c * NG + j / 4;
-                if (G < a.ngroups)
-                    a.bpart[(row * a.ngroups + G) * kBlocksPerGroup + (j % 4) * 16 + r] =
-                        make_float2(bsum[j][r] * scale, 0.0f);
-            }
+            const int64_t g0 = c * NG;   // the chunk's first group
+            const int64_t gbase = row * a.ngroups + g0;
+            if (lane < 16 * F && g0 + (lane >> 6) < a.ngroups)
+                a.bpart[gbase * kBlocksPerGroup + lane] = make_float2((&bsum[0][0])[lane] * scale, 0.0f);
             if (lane < NG * NW) {
                 const int d = lane / NW, w = lane % NW;
-                const int64_t G = c * NG + d;
-                if (G < a.ngroups) {
+                if (g0 + d < a.ngroups) {
                     float h = 0.0f;
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
                         h += (bsum[4 * d + jj][4 * w] + bsum[4 * d + jj][4 * w + 1]) +
                              (bsum[4 * d + jj][4 * w + 2] + bsum[4 * d + jj][4 * w + 3]);
-                    reinterpret_cast<float*>(a.gpart + row * a.ngroups + G)[w] = h * scale;
+                    reinterpret_cast<float*>(a.gpart + gbase)[lane] = h * scale;
                 }
             }
         }

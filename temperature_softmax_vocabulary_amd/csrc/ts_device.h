@@ -144,12 +144,14 @@ __device__ __forceinline__ void load_mask_words(const uint32_t* __restrict__ mro
                                                 uint32_t (&mw)[2]) {
     static_assert(F <= 16, "two words per lane cover at most 16 groups");
     const int l = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    const int64_t last = (V - 1) >> 5;
+    // a uniform base and 32-bit lane offsets (a row has at most 2^26 words)
+    const uint32_t* __restrict__ base = mrow + (c0 >> 5);
+    const uint32_t last = static_cast<uint32_t>(((V - 1) >> 5) - (c0 >> 5));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int j = 2 * (l >> 3) + h;
-        const int64_t idx = (c0 >> 5) + static_cast<int64_t>(j) * (NT / 8) + 8 * w + (l & 7);
-        mw[h] = mrow[idx < last ? idx : last];
+        const uint32_t off = static_cast<uint32_t>(j * (NT / 8) + 8 * w + (l & 7));
+        mw[h] = base[off < last ? off : last];
     }
 }
 
