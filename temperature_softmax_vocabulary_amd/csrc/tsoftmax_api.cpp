@@ -488,7 +488,8 @@ TS_API ts_status ts_device_errors(hipStream_t stream, uint32_t* flags) {
     uint32_t f = 0;
     if (hipMemcpy(&f, it->second.base, 4, hipMemcpyDeviceToHost) != hipSuccess) return TS_ERR_HIP;
     if (f != 0) {
-        // A timed-out wait may leave a row's counter short of zero: clear all.
+        // A timed-out wait may leave a row's slot tags out of step: clear every
+        // slot (tag 0) and flag.
         const int64_t bytes = ws_bytes(it->second.bcap, it->second.pcap);
         if (hipMemset(it->second.base, 0, static_cast<size_t>(bytes)) != hipSuccess) return TS_ERR_HIP;
     }
