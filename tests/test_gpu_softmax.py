@@ -188,3 +188,58 @@ def test_long_rows_default_plan(V):
     assert_softmax_matches(y, w.logits, w.temps, ref, what=f"V={V}")
     expect = tsv.TS_VARIANT_FUSED if V <= 256 * 16384 else tsv.TS_VARIANT_SPLIT
     assert plan[0] == expect
+
+
+@pytest.mark.parametrize("B,V", [(4, 16384), (4, 16385), (8, 262144), (8, 262148),
+                                 (2, 256 * 8192), (2, 256 * 8192 + 4)])
+def test_default_plan_at_thresholds(B, V):
+    # each side of every edge of the work-split table: rowwise up to 16384
+    # columns, fused 4096 up to 2^21 elements, fused 8192 up to 256 chunks a row
+    w = workloads.make(B, V, "quarters" if B >= 4 else "first16384")
+    plan = tsv.ts_plan(B, V)
+    print(f"[gpu] threshold B={B} V={V} plan={plan}", flush=True)
+    y = _run(w.logits, w.temps).cpu().numpy()
+    assert_softmax_matches(y, w.logits, w.temps, what=f"B={B} V={V} plan={plan}")
+    _no_device_errors()
+
+
+def _sampled_rows_match(y, w, rows):
+    """The oracle on a sample of rows; every row's invariants on the device."""
+    got = y[torch.from_numpy(rows).to(y.device)].cpu().numpy()
+    assert_softmax_matches(got, w.logits[rows], w.temps[rows], what=f"rows {rows[:4]}...")
+    assert bool(torch.isfinite(y).all())
+    dev = (y.double().sum(dim=1) - 1.0).abs().max().item()
+    assert dev <= 1e-5, dev
+    masked = torch.from_numpy(~np.isfinite(w.logits)).to(y.device)
+    assert int(torch.count_nonzero(y[masked])) == 0
+
+
+def test_many_rounds_of_the_persistent_grid():
+    # B=1024 rows of 151936: about 19 items per workgroup of the fused grid, so
+    # every workgroup waits on rows many times and the slot tags flip on every
+    # row; rows are checked against the oracle on a sample, and all rows for
+    # finiteness, exact zeros under -inf and their sums
+    w = workloads.make(1024, 151936, "quarters")
+    assert tsv.ts_plan(w.B, w.V) == (tsv.TS_VARIANT_FUSED, 8192)
+    x = torch.from_numpy(w.logits).to(DEV)
+    t = torch.from_numpy(w.temps).to(DEV)
+    print("[gpu] many rounds B=1024 V=151936", flush=True)
+    for rep in range(2):   # twice on one stream: tags carry over between calls
+        y = tsv.ts_softmax(x, t)
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(rep).choice(w.B, 24, replace=False))
+        rows[0], rows[-1] = 0, w.B - 1
+        _sampled_rows_match(y, w, rows)
+        del y
+    _no_device_errors()
+
+
+def test_rowwise_many_short_rows():
+    # the one-workgroup-per-row kernel at a large batch of short rows
+    w = workloads.make(4096, 4096, "none")
+    assert tsv.ts_plan(w.B, w.V)[0] == tsv.TS_VARIANT_ROWWISE
+    w.logits[::7, :64] = -np.inf    # leading masked columns on some rows
+    y = tsv.ts_softmax(torch.from_numpy(w.logits).to(DEV), torch.from_numpy(w.temps).to(DEV))
+    torch.cuda.synchronize()
+    rows = np.arange(0, w.B, 97)
+    _sampled_rows_match(y, w, rows)
