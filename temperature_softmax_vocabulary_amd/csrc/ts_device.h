@@ -21,9 +21,15 @@ constexpr int kWave = 64;
 constexpr float kNegInf = -__builtin_inff();
 constexpr double kLog2eD = 1.4426950408889634073599246810019;
 
-// k = log2(e) / T, formed in double and rounded once to float.
+// k = log2(e) / T, formed in double and rounded once to float. A temperature
+// so small (denormal) that k would overflow takes the largest float instead:
+// (x - max) k is then 0 at the row's max and -inf or far below -126 elsewhere,
+// the one-hot limit of the softmax, where an infinite k would give 0 * inf =
+// NaN at the max. Every normal temperature is unaffected.
 __device__ __forceinline__ float exp2_scale(float T) {
-    return static_cast<float>(kLog2eD / static_cast<double>(T));
+    constexpr double kFltMax = 3.4028234663852886e38;
+    const double k = kLog2eD / static_cast<double>(T);
+    return static_cast<float>(k < kFltMax ? k : kFltMax);
 }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -243,3 +243,22 @@ def test_rowwise_many_short_rows():
     torch.cuda.synchronize()
     rows = np.arange(0, w.B, 97)
     _sampled_rows_match(y, w, rows)
+
+
+def test_extreme_temperatures():
+    # a denormal temperature (k = log2(e)/T beyond the float range) gives the
+    # one-hot limit, as the float64 definition does; a huge one the uniform
+    # limit; both through every split
+    rng = np.random.default_rng(41)
+    V = 20000
+    x = (rng.standard_normal((5, V)) * 4).astype(np.float32)
+    x[1, 100:200] = -np.inf
+    x[3, 7] = x[3].max() + np.float32(0.5)
+    t = np.array([1e-45, 2e-39, 1e-30, 1e30, 3.4e38], np.float32)
+    ref = softmax_ref(x, t)
+    for v, c in SPLITS:
+        y = _run(x, t, v, c).cpu().numpy()
+        assert_softmax_matches(y, x, t, ref, what=f"extreme T {v}/{c}")
+        for r in (0, 1, 2):
+            assert y[r].max() == 1.0 and np.count_nonzero(y[r]) == 1, (v, c, r)
+    _no_device_errors()
