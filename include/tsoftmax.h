@@ -88,8 +88,10 @@ typedef enum ts_variant {
  *          or temps is rejected.
  * Result : for a row with at least one finite logit every output is finite,
  *          a -inf logit gives exactly 0, and the row sums to 1 within float32
- *          rounding. No alignment is required; 16-byte aligned pointers with
- *          V % 4 == 0 take the vector-load path.
+ *          rounding. No alignment beyond float's 4 bytes is required: rows
+ *          are read and written 16 bytes at a time either way (aligned when
+ *          logits and out are 16-byte aligned and V % 4 == 0, unaligned
+ *          otherwise, the row's last partial float4 element by element).
  * Errors : TS_ERR_INVALID_ARGUMENT for B < 0, V < 1, V > INT32_MAX,
  *          B*V*4 not addressable, a NULL pointer when B > 0, or an illegal
  *          overlap. B == 0 is a no-op returning TS_OK.

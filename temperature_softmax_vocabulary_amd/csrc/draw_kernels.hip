@@ -74,7 +74,7 @@ __device__ __forceinline__ void block_reduce_n(float (&v)[N], float (*lds)[NW]) 
 // each), so group G = GPW h + j / 4 and its block b = 16 (j % 4) + t / 16 is
 // one row of 16 lanes.
 // ---------------------------------------------------------------------------
-template <bool VEC, int KIND, int GPW>
+template <int LD, int KIND, int GPW>
 __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
     __shared__ float red[GPW][DW];   // (logits only)
     constexpr int F = 4 * GPW;
@@ -90,8 +90,9 @@ __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
             const int64_t c0 = G0 * kDrawGroup;
             const uint32_t* mrow = draw_mask_row(a, row);
             uint32_t mw[2];
-            issue_chunk_loads<DT, F, VEC, true>(a.x + row * a.V, c0, a.V, x);
+            issue_chunk_loads<DT, F, LD, true>(a.x + row * a.V, c0, a.V, x);
             if (mrow) load_mask_words<DT, F>(mrow, c0, a.V, mw);
+            if constexpr (LD == kLdUnaligned) shift_tail_group<DT, F>(c0, a.V, x);
             fill_past_end<DT, F>(c0, a.V, x, kNegInf);
             if (mrow) apply_mask_words<DT, F>(c0, a.V, mw, x);
         }
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
         for (int d = 0; d < GPW; ++d)
             if (t == 0 && G0 + d < a.ngroups) a.gpart[row * a.ngroups + G0 + d] = make_float4(gm[d], gl[d], 0.0f, 0.0f);
     } else {
-        issue_chunk_loads<DT, F, VEC, true>(a.x + row * a.V, G0 * kDrawGroup, a.V, x);
+        issue_chunk_loads<DT, F, LD, true>(a.x + row * a.V, G0 * kDrawGroup, a.V, x);
+        if constexpr (LD == kLdUnaligned) shift_tail_group<DT, F>(G0 * kDrawGroup, a.V, x);
         fill_past_end<DT, F>(G0 * kDrawGroup, a.V, x, 0.0f);
         float gs[GPW];
 #pragma unroll
@@ -271,20 +273,31 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
 // call fills the device, else one.
 constexpr int kPartialsGPW = 2;
 
-template <bool VEC, int GPW>
+template <int LD, int GPW>
 hipError_t partials_impl(const DrawArgs& a, int kind, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(a.B * ((a.ngroups + GPW - 1) / GPW)));
-    if (kind == kDrawLogits) hipLaunchKernelGGL((ts_draw_partials<VEC, kDrawLogits, GPW>), grid, dim3(DT), 0, s, a);
-    else hipLaunchKernelGGL((ts_draw_partials<VEC, kDrawProbs, GPW>), grid, dim3(DT), 0, s, a);
+    if (kind == kDrawLogits) hipLaunchKernelGGL((ts_draw_partials<LD, kDrawLogits, GPW>), grid, dim3(DT), 0, s, a);
+    else hipLaunchKernelGGL((ts_draw_partials<LD, kDrawProbs, GPW>), grid, dim3(DT), 0, s, a);
     return hipGetLastError();
+}
+
+template <int GPW>
+hipError_t partials_ld(const DrawArgs& a, int ld, int kind, hipStream_t s) {
+    switch (ld) {
+        case kLdAligned: return partials_impl<kLdAligned, GPW>(a, kind, s);
+        case kLdUnaligned: return partials_impl<kLdUnaligned, GPW>(a, kind, s);
+        case kLdScalar: return partials_impl<kLdScalar, GPW>(a, kind, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_draw_partials(const DrawArgs& a, bool vec, int kind, hipStream_t s) {
+hipError_t launch_draw_partials(const DrawArgs& a, int ld, int kind, hipStream_t s) {
+    // the unaligned loads need a row of at least 4 columns
+    if (ld == kLdUnaligned && a.V < 4) ld = kLdScalar;
     const bool wide = a.B * a.ngroups >= 2048;
-    if (wide) return vec ? partials_impl<true, kPartialsGPW>(a, kind, s) : partials_impl<false, kPartialsGPW>(a, kind, s);
-    return vec ? partials_impl<true, 1>(a, kind, s) : partials_impl<false, 1>(a, kind, s);
+    return wide ? partials_ld<kPartialsGPW>(a, ld, kind, s) : partials_ld<1>(a, ld, kind, s);
 }
 
 hipError_t launch_draw_resolve(const DrawArgs& a, int kind, hipStream_t s) {

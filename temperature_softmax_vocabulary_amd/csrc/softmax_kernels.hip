@@ -289,7 +289,7 @@ __global__ __launch_bounds__(RT) void ts_rowwise_resident(SoftmaxArgs a) {
 
 // ---------------------------------------------------------------------------
 // rowwise, streaming: online (m, l) per lane over the row, a workgroup
-// combine, then a write sweep. Tile = RT lanes x U float4 (or 4U scalars).
+// combine, then a write sweep. Tile = RT lanes x U float4.
 // ---------------------------------------------------------------------------
 template <int RT, bool VEC>
 __global__ __launch_bounds__(RT) void ts_rowwise_stream(SoftmaxArgs a) {

@@ -13,9 +13,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ts_launch.h"   // kLd*: how a one-shot kernel loads a chunk
+
 namespace tsk {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+// A float4 at a 4-byte aligned address: gfx950 serves one unaligned 16-byte
+// global load or store for it (loads at full speed, stores within a few per
+// cent of aligned ones, measured on MI355X).
+typedef float f4u __attribute__((ext_vector_type(4))) __attribute__((aligned(4)));
 
 constexpr int kWave = 64;
 constexpr float kNegInf = -__builtin_inff();
@@ -121,11 +127,13 @@ __device__ __forceinline__ float block_reduce(float v, float* lds) {
 // Chunk access. A chunk is C = NT * 4 * F consecutive columns of one row, in F
 // groups of NT * 4 columns. Lane t of the workgroup owns the 4 consecutive
 // columns c0 + (j * NT + t) * 4 + e, e in [0, 4), of every group j, held in
-// x[4 j + e]; within a group, lane order is column order. Vector path (16-byte
-// aligned row, V % 4 == 0): one float4 load per group, so each wave64 load
-// instruction covers 1 KiB of contiguous memory. Scalar path: four bounds-
-// checked 4-byte loads per group. Columns at or past V read as `fill` (-inf
-// for logits: they add nothing to a max or to a sum of exponentials).
+// x[4 j + e]; within a group, lane order is column order. One float4 load per
+// group, so each wave64 load instruction covers 1 KiB of contiguous memory:
+// aligned (VEC: a 16-byte aligned row start and V % 4 == 0) or unaligned (any
+// 4-byte aligned row, e.g. an odd V), where the row's last float4, when V % 4
+// != 0, is partial and is read element by element. Columns at or past V read
+// as `fill` (-inf for logits: they add nothing to a max or to a sum of
+// exponentials).
 // ---------------------------------------------------------------------------
 // allowed-id bitmask of one row: bit (j % 32) of word j / 32, 1 = allowed. A
 // lane's 4 columns of a group share one word (4 divides 32), so the mask costs
@@ -194,21 +202,37 @@ __device__ __forceinline__ void fill_past_end(int64_t c0, int64_t V, float (&x)[
 
 // Issues the chunk's loads: every one before any value is used, none under a
 // branch (a branch around a load makes the compiler wait for it at the join).
-// Addresses are the chunk's start (uniform) plus a 32-bit lane offset; a lane
-// past V reads the chunk's first column instead, which always exists, and
-// holds garbage until fill_past_end replaces it.
-template <int NT, int F, bool VEC, bool NT_LOAD>
+// Addresses are the chunk's start (uniform) plus a 32-bit lane offset.
+//  kLdAligned: a lane past V reads the chunk's first float4 instead, which
+//    always exists, and holds garbage until fill_past_end replaces it.
+//  kLdUnaligned (V >= 4): a float4 that is not wholly inside the row is read
+//    from the row's last 4 columns instead (the float4 ending at V, which may
+//    start in the chunk before); shift_tail_group then moves the lane's own
+//    columns into place, and fill_past_end replaces the rest.
+//  kLdScalar: each column alone, at the chunk's first column when past V.
+template <int NT, int F, int LD, bool NT_LOAD>
 __device__ __forceinline__ void issue_chunk_loads(const float* __restrict__ row, int64_t c0, int64_t V,
                                                   float (&x)[4 * F]) {
     const int t = threadIdx.x;
     const float* __restrict__ base = row + c0;
     const int64_t left = V - c0;   // columns from the chunk's start to the row's end (> 0)
-    if constexpr (VEC) {
+    if constexpr (LD == kLdAligned) {
 #pragma unroll
         for (int j = 0; j < F; ++j) {
             const uint32_t off = static_cast<uint32_t>((j * NT + t) * 4);
             const f4* p = reinterpret_cast<const f4*>(base + (off < left ? off : 0u));
             f4 v;
+            if constexpr (NT_LOAD) v = __builtin_nontemporal_load(p);
+            else v = *p;
+            x[4 * j + 0] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
+        }
+    } else if constexpr (LD == kLdUnaligned) {
+        const int64_t last = left - 4;   // start of the row's last 4 columns, from c0 (>= -c0: V >= 4)
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const int64_t off = (j * NT + t) * 4;
+            const f4u* p = reinterpret_cast<const f4u*>(base + (off < last ? off : last));
+            f4u v;
             if constexpr (NT_LOAD) v = __builtin_nontemporal_load(p);
             else v = *p;
             x[4 * j + 0] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
@@ -224,6 +248,25 @@ __device__ __forceinline__ void issue_chunk_loads(const float* __restrict__ row,
                 else x[4 * j + e] = *p;
             }
         }
+    }
+}
+
+// After kLdUnaligned loads: the lane whose float4 straddles V read the row's
+// last 4 columns, starting d = 1..3 columns before its own first column; its
+// columns below V are elements d .. 3 of what it read. (Columns at or past V
+// are left for fill_past_end.)
+template <int NT, int F>
+__device__ __forceinline__ void shift_tail_group(int64_t c0, int64_t V, float (&x)[4 * F]) {
+    const int t = threadIdx.x;
+    const int64_t last = V - c0 - 4;
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+        const int64_t off = (j * NT + t) * 4;
+        const int64_t d = off < last ? 0 : off - last;
+        const float w0 = x[4 * j], w1 = x[4 * j + 1], w2 = x[4 * j + 2], w3 = x[4 * j + 3];
+        x[4 * j + 0] = d == 0 ? w0 : (d == 1 ? w1 : (d == 2 ? w2 : w3));
+        x[4 * j + 1] = d == 0 ? w1 : (d == 1 ? w2 : w3);
+        x[4 * j + 2] = d == 0 ? w2 : w3;
     }
 }
 
@@ -252,15 +295,24 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_
 #pragma unroll
         for (int j = 0; j < F; ++j) {
             const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+            float v[4] = {fill, fill, fill, fill};
+            if (col + 3 < V) {   // wholly inside the row: one unaligned 16-byte load
+                const f4u* p = reinterpret_cast<const f4u*>(row + col);
+                f4u q;
+                if constexpr (NT_LOAD) q = __builtin_nontemporal_load(p);
+                else q = *p;
+                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+            } else {             // the row's last, partial float4 (or past V)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = fill;
-                if (col + e < V) {
-                    if constexpr (NT_LOAD) v = __builtin_nontemporal_load(row + col + e);
-                    else v = row[col + e];
+                for (int e = 0; e < 3; ++e) {
+                    if (col + e < V) {
+                        if constexpr (NT_LOAD) v[e] = __builtin_nontemporal_load(row + col + e);
+                        else v[e] = row[col + e];
+                    }
                 }
-                x[4 * j + e] = v;
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * j + e] = v[e];
         }
     }
     if (mrow) {
@@ -289,11 +341,18 @@ __device__ __forceinline__ void store_chunk(float* __restrict__ row, int64_t c0,
 #pragma unroll
         for (int j = 0; j < F; ++j) {
             const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
+            if (col + 3 < V) {   // wholly inside the row: one unaligned 16-byte store
+                f4u v = {y[4 * j + 0], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]};
+                f4u* p = reinterpret_cast<f4u*>(row + col);
+                if constexpr (NT_STORE) __builtin_nontemporal_store(v, p);
+                else *p = v;
+            } else {             // the row's last, partial float4 (or past V)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (col + e < V) {
-                    if constexpr (NT_STORE) __builtin_nontemporal_store(y[4 * j + e], row + col + e);
-                    else row[col + e] = y[4 * j + e];
+                for (int e = 0; e < 3; ++e) {
+                    if (col + e < V) {
+                        if constexpr (NT_STORE) __builtin_nontemporal_store(y[4 * j + e], row + col + e);
+                        else row[col + e] = y[4 * j + e];
+                    }
                 }
             }
         }

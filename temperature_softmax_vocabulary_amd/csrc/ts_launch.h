@@ -62,6 +62,12 @@ hipError_t launch_fused(const SoftmaxArgs& a, int F, bool vec, int mode, int64_t
 hipError_t fused_resident_capacity(int F, bool vec, int mode, int64_t* cap);
 hipError_t launch_rowwise(const SoftmaxArgs& a, bool vec, hipStream_t s);
 
+// How a one-shot kernel loads a chunk (issue_chunk_loads in ts_device.h):
+// four 4-byte loads per group of 4 columns (rows of fewer than 4 columns), one
+// unaligned float4 per group (any other row), one aligned float4 per group (a
+// 16-byte aligned row start and V % 4 == 0).
+constexpr int kLdScalar = 0, kLdUnaligned = 1, kLdAligned = 2;
+
 // Token draws (draw_kernels.hip).
 constexpr int kDrawLogits = 0, kDrawProbs = 1;
 struct DrawArgs {
@@ -80,8 +86,9 @@ struct DrawArgs {
     int64_t K;
     int64_t ngroups;          // ceil(V / kDrawGroup)
 };
-// Group and block partials over the whole of x (one read), one group per workgroup.
-hipError_t launch_draw_partials(const DrawArgs& a, bool vec, int kind, hipStream_t s);
+// Group and block partials over the whole of x (one read), one group per
+// workgroup; ld: a kLd* for x's rows.
+hipError_t launch_draw_partials(const DrawArgs& a, int ld, int kind, hipStream_t s);
 // One wave per (row, target): the target's group, then its block, then its id.
 hipError_t launch_draw_resolve(const DrawArgs& a, int kind, hipStream_t s);
 

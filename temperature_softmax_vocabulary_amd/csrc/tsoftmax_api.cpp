@@ -362,9 +362,9 @@ ts_status launch_draw(int kind, const float* x, const float* temps, const uint32
     d.ngroups = cdiv(V, tsk::kDrawGroup);
     d.gpart = reinterpret_cast<float4*>(v.part);
     d.bpart = v.part + 2 * B * d.ngroups;
-    const bool vec = aligned16(x) && (V % 4 == 0);
+    const int ld = aligned16(x) && (V % 4 == 0) ? tsk::kLdAligned : tsk::kLdUnaligned;
     if (!partials_done) {
-        hipError_t e = tsk::launch_draw_partials(d, vec, kind, stream);
+        hipError_t e = tsk::launch_draw_partials(d, ld, kind, stream);
         if (e != hipSuccess) return hip_status(e);
     }
     return hip_status(tsk::launch_draw_resolve(d, kind, stream));

@@ -1,0 +1,124 @@
+"""Rows that are not 16-byte aligned: an odd vocabulary (V % 4 != 0) or a
+pointer 4 bytes past a 16-byte boundary.
+
+Such rows are read and written with unaligned 16-byte accesses, the row's last
+partial float4 element by element. Every value sits in the same lane and goes
+through the same arithmetic as on the aligned path, so the same data must give
+bitwise the same probabilities and the same ids whichever path reads it. Odd
+vocabularies are checked against the float64 oracle, with -inf at the row's
+last columns: the columns the partial float4 holds (the method's masked
+entries, pull-request page "fix(kernel): avoid nan in triton sampling softmax
+when a chunk starts with -inf", bug and fix paragraphs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import temperature_softmax_vocabulary_amd as tsv
+from oracle import softmax_ref
+from temperature_softmax_vocabulary_amd import workloads
+from tests.parity import assert_ids_valid, assert_softmax_matches
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SPLITS = [(tsv.TS_VARIANT_SPLIT, c) for c in tsv.CHUNKS] + \
+         [(tsv.TS_VARIANT_FUSED, c) for c in tsv.CHUNKS] + [(tsv.TS_VARIANT_ROWWISE, 0)]
+SPLIT_IDS = [f"{tsv.VARIANT_NAMES[v]}-{c}" for v, c in SPLITS]
+
+
+def _offset(a: np.ndarray, fill=0.0):
+    """A device copy of `a` that starts 4 bytes past a 16-byte boundary."""
+    base = torch.full((a.size + 4,), fill, dtype=torch.float32 if a.dtype == np.float32 else torch.int32,
+                      device=DEV)
+    t = base[1: 1 + a.size].view(a.shape)
+    t.copy_(torch.from_numpy(a))
+    return t, base
+
+
+def _empty_offset(shape):
+    n = int(np.prod(shape))
+    base = torch.full((n + 4,), 7.0, dtype=torch.float32, device=DEV)
+    return base[1: 1 + n].view(shape), base
+
+
+@pytest.mark.parametrize("variant,chunk", SPLITS, ids=SPLIT_IDS)
+def test_offset_rows_bitwise_equal_aligned(variant, chunk):
+    w = workloads.make_config("B8_V201088_block_and_head")
+    t = torch.from_numpy(w.temps).to(DEV)
+    xa = torch.from_numpy(w.logits).to(DEV)
+    ya = tsv.ts_softmax_variant(xa, t, variant, chunk)
+    xu, _ = _offset(w.logits)
+    yu, ybase = _empty_offset((w.B, w.V))
+    tsv.ts_softmax_variant(xu, t, variant, chunk, out=yu)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yu), (variant, chunk)
+    b = ybase.cpu().numpy()
+    assert b[0] == 7.0 and np.all(b[1 + w.B * w.V:] == 7.0), "wrote outside out"
+
+
+@pytest.mark.parametrize("variant,chunk", SPLITS, ids=SPLIT_IDS)
+@pytest.mark.parametrize("r", [1, 2, 3])
+def test_odd_vocabulary_tails(variant, chunk, r):
+    # V % 4 == r: the last float4 of every row is partial. Rows: masked up to the
+    # partial float4 (its columns hold the only finite logits), masked on the
+    # partial float4, finite only at the very last column, unmasked.
+    V = 2 * 8192 + 4 * 37 + r
+    rng = np.random.default_rng(100 + r)
+    x = (rng.standard_normal((6, V)) * 4).astype(np.float32)
+    NEG = np.float32(-np.inf)
+    tail = V - r
+    x[0, :tail] = NEG
+    x[1, tail:] = NEG
+    x[2, :] = NEG
+    x[2, V - 1] = np.float32(1.5)
+    x[3, tail - 4: tail] = NEG
+    x[4, 0] = x[4].max() + np.float32(50.0)
+    t = np.array([0.5, 0.8, 1.0, 1.2, 0.7, 1.4], np.float32)
+    y = tsv.ts_softmax_variant(torch.from_numpy(x).to(DEV), torch.from_numpy(t).to(DEV), variant, chunk)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert_softmax_matches(got, x, t, what=f"V={V} {variant}/{chunk}")
+    assert got[2, V - 1] == 1.0
+
+
+@pytest.mark.parametrize("V", [50257, 151937, 262143, 7])
+def test_odd_vocabulary_default_plan_and_draws(V):
+    w = workloads.make(16, V, "quarters" if V > 20000 else "none")
+    ref = softmax_ref(w.logits, w.temps)
+    x, t, u = (torch.from_numpy(a).to(DEV) for a in (w.logits, w.temps, w.uniforms))
+    y = tsv.ts_softmax(x, t)
+    ids_p = tsv.ts_sample(y, u)
+    ids_l, _ = tsv.ts_softmax_sample(x, t, u)
+    ids_w, p2 = tsv.ts_softmax_sample(x, t, u, probs_out=True)
+    torch.cuda.synchronize()
+    assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, ref, what=f"V={V}")
+    # (with the draw the softmax may run another chunk size: equal to rounding)
+    assert_softmax_matches(p2.cpu().numpy(), w.logits, w.temps, ref, what=f"V={V} with draw")
+    for ids, what in ((ids_p, "sample"), (ids_l, "ids only"), (ids_w, "with probs")):
+        assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), w.uniforms, what=f"V={V} {what}")
+    assert tsv.ts_device_errors() == 0
+
+
+def test_offset_draws_equal_aligned():
+    # the draw's partials read offset rows with unaligned loads: same ids
+    w = workloads.make_config("B64_V262144_masked_quarters")
+    p32 = softmax_ref(w.logits, w.temps).astype(np.float32)
+    u = torch.from_numpy(w.uniforms).to(DEV)
+    ids_a = tsv.ts_sample(torch.from_numpy(p32).to(DEV), u)
+    pu, _ = _offset(p32)
+    ids_u = tsv.ts_sample(pu, u)
+    t = torch.from_numpy(w.temps).to(DEV)
+    la = tsv.ts_softmax_sample(torch.from_numpy(w.logits).to(DEV), t, u)[0]
+    xu, _ = _offset(w.logits)
+    lu = tsv.ts_softmax_sample(xu, t, u)[0]
+    bits = workloads.make_allowed(w).view(np.int32)
+    xm = workloads.unmasked_logits(w)
+    ma = tsv.ts_softmax_sample(torch.from_numpy(xm).to(DEV), t, u, allowed=torch.from_numpy(bits).to(DEV))[0]
+    xmu, _ = _offset(xm)
+    mu = tsv.ts_softmax_sample(xmu, t, u, allowed=torch.from_numpy(bits).to(DEV))[0]
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_u)
+    assert torch.equal(la, lu)
+    assert torch.equal(ma, mu)
+    assert torch.equal(la, ma)   # the bitmask is the -inf pattern of the logits
+    assert_ids_valid(ids_u.cpu().numpy(), p32, w.uniforms)
