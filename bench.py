@@ -294,6 +294,49 @@ def cpu_baseline(w, target_s: float):
                       f"one thread: {r1} calls in {e1:.1f} s, {g1:.3f} GB/s, us/call {e1 / r1 * 1e6:.0f}"}
 
 
+SWEEP_SHAPES = [(B, V) for V in (151936, 201088, 262144) for B in (1, 3, 8, 16, 32, 64, 128, 256)]
+
+
+def sweep(torch, tsv, workloads, dev, shapes, steps: int) -> str:
+    """Cold µs per call of every work split and chunk size, and of a copy of
+    the same bytes, for each (B, V): the measurements behind the work-split
+    table. Inputs rotate over >= 1 GiB as in the headline run; eager calls.
+    Returns a markdown table (the plan's choice marked with *)."""
+    splits = [(tsv.TS_VARIANT_FUSED, c) for c in tsv.CHUNKS] + \
+             [(tsv.TS_VARIANT_SPLIT, c) for c in tsv.CHUNKS] + [(tsv.TS_VARIANT_ROWWISE, 0)]
+    names = [f"{tsv.VARIANT_NAMES[v]} {c}" if c else tsv.VARIANT_NAMES[v] for v, c in splits]
+    lines = ["| B | V | " + " | ".join(names) + " | copy | plan/best |",
+             "|---|---|" + "---|" * (len(splits) + 2)]
+    for B, V in shapes:
+        w = workloads.make(B, V, "quarters")
+        nsets = max(2, math.ceil(COLD_FOOTPRINT / (2 * B * V * 4)))
+        xs = [torch.from_numpy(w.logits).to(dev) for _ in range(nsets)]
+        t = torch.from_numpy(w.temps).to(dev)
+        ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
+        tsv.ts_reserve(B, V)
+        plan = tsv.ts_plan(B, V)
+        cells, best = [], (float("inf"), None)
+        for v, c in splits:
+            if v == tsv.TS_VARIANT_FUSED and -(-V // c) > 256:
+                cells.append("—")
+                continue
+            def call(i, v=v, c=c):
+                tsv.ts_softmax_variant(xs[i % nsets], t, v, c, out=ys[i % nsets])
+            for i in range(10):
+                call(i)
+            us = _elapsed_us(torch, call, steps)
+            mark = "*" if (v, c) == tuple(plan) or (v == plan[0] == tsv.TS_VARIANT_ROWWISE) else ""
+            cells.append(f"{us:.2f}{mark}")
+            if us < best[0]:
+                best = (us, (v, c))
+        cp = _elapsed_us(torch, lambda i: tsv.ts_copy_f32(xs[i % nsets], ys[i % nsets]), steps)
+        pick = f"{tsv.VARIANT_NAMES[plan[0]]} {plan[1]} / {tsv.VARIANT_NAMES[best[1][0]]} {best[1][1]}"
+        lines.append(f"| {B} | {V} | " + " | ".join(cells) + f" | {cp:.2f} | {pick} |")
+        print(lines[-1], file=sys.stderr, flush=True)
+        del xs, ys
+    return "\n".join(lines)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,6 +351,9 @@ def main(argv=None) -> int:
                     help="side measurements after the timed region: all, only the copy "
                          "(the counter runs' calibration), or none")
     ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the JSON line: a table of cold µs per call for every work split "
+                         "and chunk size over B in {1..256} x V in {151936, 201088, 262144}")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--profile-command", default="python3 bench.py --steps 200 --warmup 20 --no-cpu-baseline",
@@ -353,6 +399,9 @@ def main(argv=None) -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        print(sweep(torch, tsv, workloads, dev, SWEEP_SHAPES, min(args.steps, 200)), flush=True)
+        return 0
     w = workloads.make_config(args.workload)
     B, V = w.B, w.V
     bytes_per_call = 2 * B * V * 4
