@@ -67,7 +67,12 @@ typedef enum ts_status {
  *                        registers while the per-chunk partials are exchanged
  *                        through tagged per-row slots in the stream's
  *                        workspace, then writes the probs. Reads the logits
- *                        once. Rows of at most 256 chunks. */
+ *                        once. Rows of at most 256 chunks. Its grid is sized
+ *                        to what the device holds at once; should the device be
+ *                        shared with another kernel that waits on its own
+ *                        co-resident workgroups, a row's wait can run out
+ *                        (TS_ERR_SYNC_TIMEOUT from ts_device_errors). SPLIT
+ *                        and ROWWISE never wait. */
 typedef enum ts_variant {
     TS_VARIANT_AUTO = 0,
     TS_VARIANT_SPLIT = 1,

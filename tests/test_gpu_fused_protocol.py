@@ -98,3 +98,24 @@ def test_fused_rejects_rows_with_too_many_chunks():
     y = tsv.ts_softmax(x, t)          # the default plan picks a legal split
     torch.cuda.synchronize()
     assert np.allclose(y.cpu().numpy(), 1.0 / 300000, rtol=1e-6)
+
+
+def test_concurrent_full_grids_on_two_streams():
+    # Two calls whose grids each fill the device (B=64 x 262144: 1024
+    # workgroups apiece), issued on two streams at once, ten times. Their
+    # workgroups may share the device; every row must still complete (no
+    # bounded wait runs out) and give the single-stream result bit for bit.
+    w, x1, t = _case(64, 262144, 9)
+    x2 = x1.clone()
+    ref = tsv.ts_softmax(x1, t)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    tsv.ts_reserve(64, 262144, device=DEV, stream=s1)
+    tsv.ts_reserve(64, 262144, device=DEV, stream=s2)
+    for it in range(10):
+        a = tsv.ts_softmax(x1, t, stream=s1)
+        b = tsv.ts_softmax(x2, t, stream=s2)
+        torch.cuda.synchronize()
+        assert tsv.ts_device_errors(device=DEV, stream=s1) == 0, it
+        assert tsv.ts_device_errors(device=DEV, stream=s2) == 0, it
+        assert torch.equal(a, ref) and torch.equal(b, ref), it
