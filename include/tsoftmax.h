@@ -199,6 +199,11 @@ ts_status ts_softmax_sample(const float* logits, const float* temps, const uint3
  * V <= max_V on `stream`, so that those calls allocate nothing (needed
  * before capturing them into a HIP graph). Allocates and clears device
  * memory; must not itself be called while `stream` is capturing.
+ * A graph captured on `stream` keeps using that stream's workspace wherever it
+ * is replayed: its replays must not overlap other work on the same workspace
+ * (calls on `stream`, or another replay of a graph captured on it), exactly as
+ * two calls on one stream never overlap. The workspace lives until the process
+ * ends.
  */
 ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream);
 

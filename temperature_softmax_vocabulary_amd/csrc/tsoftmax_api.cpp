@@ -11,6 +11,7 @@
 #include <tuple>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/tsoftmax.h"
 #include "../../include/tsoftmax_measure.h"
@@ -48,11 +49,18 @@ bool sizes_ok(int64_t B, int64_t V) {
 //   [0, 256)                                   flags (uint32 at offset 0)
 //   [256, 256 + 8 kSlotStride Bcap kSlotSets)  slots[kSlotSets][Bcap][kSlotStride]
 //   [aligned 256, + 8 Pcap)                    part[Pcap] (float2, split)
+// An outgrown allocation is retired, never freed: a graph captured on the
+// stream may still point at it, and work queued before the growth may still
+// use it. Growth is geometric, so a stream retires only a few.
 // ----------------------------------------------------------------------------
-struct Workspace {
+struct Alloc {
     void* base = nullptr;
     int64_t bcap = 0;   // rows
     int64_t pcap = 0;   // partials
+};
+
+struct Workspace : Alloc {
+    std::vector<Alloc> retired;
 };
 
 struct WsView {
@@ -69,7 +77,7 @@ int64_t ws_bytes(int64_t bcap, int64_t pcap) {
     return align256(256 + slot_bytes(bcap)) + 8 * pcap;
 }
 
-WsView ws_view(const Workspace& w) {
+WsView ws_view(const Alloc& w) {
     char* b = static_cast<char*>(w.base);
     WsView v;
     v.err = reinterpret_cast<uint32_t*>(b);
@@ -103,24 +111,21 @@ ts_status ws_get(hipStream_t stream, int64_t need_b, int64_t need_p, Workspace**
     e = hipStreamIsCapturing(stream, &cap);
     if (e != hipSuccess) return TS_ERR_HIP;
     if (cap != hipStreamCaptureStatusNone) return TS_ERR_NOT_RESERVED;
-    const int64_t nb = need_b > w.bcap ? need_b : w.bcap;
-    const int64_t np = need_p > w.pcap ? need_p : w.pcap;
-    if (w.base) {
-        // Work already queued on this stream may still use the old buffer.
-        e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return TS_ERR_HIP;
-        (void)hipFree(w.base);
-        w = Workspace{};
-    }
+    // at least double what grows, so that few allocations are ever retired
+    int64_t nb = w.bcap, np = w.pcap;
+    if (need_b > nb) nb = need_b > 2 * w.bcap ? need_b : 2 * w.bcap;
+    if (need_p > np) np = need_p > 2 * w.pcap ? need_p : 2 * w.pcap;
     void* p = nullptr;
     const int64_t bytes = ws_bytes(nb, np);
     e = hipMalloc(&p, static_cast<size_t>(bytes));
     if (e != hipSuccess) return e == hipErrorOutOfMemory ? TS_ERR_OUT_OF_MEMORY : TS_ERR_HIP;
+    // cleared in stream order, before any later call on the stream uses it
     e = hipMemsetAsync(p, 0, static_cast<size_t>(bytes), stream);
     if (e != hipSuccess) {
         (void)hipFree(p);
         return TS_ERR_HIP;
     }
+    if (w.base) w.retired.push_back(Alloc{w.base, w.bcap, w.pcap});
     w.base = p;
     w.bcap = nb;
     w.pcap = np;
@@ -485,16 +490,21 @@ TS_API ts_status ts_device_errors(hipStream_t stream, uint32_t* flags) {
     auto it = g_ws.find({dev, stream});
     if (it == g_ws.end() || !it->second.base) return TS_OK;
     if (hipStreamSynchronize(stream) != hipSuccess) return TS_ERR_HIP;
-    uint32_t f = 0;
-    if (hipMemcpy(&f, it->second.base, 4, hipMemcpyDeviceToHost) != hipSuccess) return TS_ERR_HIP;
-    if (f != 0) {
-        // A timed-out wait may leave a row's slot tags out of step: clear every
-        // slot (tag 0) and flag.
-        const int64_t bytes = ws_bytes(it->second.bcap, it->second.pcap);
-        if (hipMemset(it->second.base, 0, static_cast<size_t>(bytes)) != hipSuccess) return TS_ERR_HIP;
+    uint32_t all = 0;
+    std::vector<Alloc> allocs = it->second.retired;   // (graphs may still write to these)
+    allocs.push_back(it->second);
+    for (const Alloc& a : allocs) {
+        uint32_t f = 0;
+        if (hipMemcpy(&f, a.base, 4, hipMemcpyDeviceToHost) != hipSuccess) return TS_ERR_HIP;
+        if (f != 0) {
+            // A timed-out wait may leave a row's slot tags out of step: clear
+            // every slot (tag 0) and flag.
+            if (hipMemset(a.base, 0, static_cast<size_t>(ws_bytes(a.bcap, a.pcap))) != hipSuccess) return TS_ERR_HIP;
+        }
+        all |= f;
     }
-    *flags = f;
-    return (f & 1u) ? TS_ERR_SYNC_TIMEOUT : TS_OK;
+    *flags = all;
+    return (all & 1u) ? TS_ERR_SYNC_TIMEOUT : TS_OK;
 }
 
 TS_API const char* ts_status_string(ts_status s) {

@@ -72,3 +72,45 @@ def test_capture_without_reserve_is_refused(variant, chunk):
         except tsv.TsError as e:
             err = e
     assert err is not None and err.status == tsv.TS_ERR_NOT_RESERVED
+
+
+def test_graph_survives_later_workspace_growth():
+    # A graph captured on a stream keeps pointing at that stream's workspace.
+    # A later, larger eager call on the same stream grows the workspace; the
+    # outgrown one stays allocated, so the graph's replays still run on it,
+    # interleaved with eager calls on the new one.
+    B, V, K = 8, 201088, 16
+    s = torch.cuda.Stream(device=DEV)
+    tsv.ts_reserve(B, V, device=DEV, stream=s)
+    x = torch.zeros((B, V), dtype=torch.float32, device=DEV)
+    t = torch.ones((B,), dtype=torch.float32, device=DEV)
+    u = torch.zeros((B, K), dtype=torch.float32, device=DEV)
+    y = torch.empty_like(x)
+    ids = torch.empty((B, K), dtype=torch.int32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        tsv.ts_softmax(x, t, out=y)
+        tsv.ts_sample(y, u, out_ids=ids)
+    s.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        tsv.ts_softmax(x, t, out=y)
+        tsv.ts_sample(y, u, out_ids=ids)
+    big = workloads.make(64, 262144, "quarters", seed=7)
+    xb, tb = torch.from_numpy(big.logits).to(DEV), torch.from_numpy(big.temps).to(DEV)
+    for rep in range(3):
+        # a larger call on the capture stream: the first one grows its workspace
+        with torch.cuda.stream(s):
+            yb = tsv.ts_softmax(xb, tb, stream=s)
+        s.synchronize()
+        assert_softmax_matches(yb.cpu().numpy(), big.logits, big.temps, what=f"eager {rep}")
+        w = workloads.make(B, V, "quarters", K=K, seed=2000 + rep)
+        x.copy_(torch.from_numpy(w.logits))
+        t.copy_(torch.from_numpy(w.temps))
+        u.copy_(torch.from_numpy(w.uniforms))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert_softmax_matches(got, w.logits, w.temps, what=f"replay {rep}")
+        assert_ids_valid(ids.cpu().numpy(), got, w.uniforms, what=f"replay {rep}")
+    assert tsv.ts_device_errors(device=DEV, stream=s) == 0
