@@ -337,6 +337,77 @@ def sweep(torch, tsv, workloads, dev, shapes, steps: int) -> str:
     return "\n".join(lines)
 
 
+PAGE_SHAPES = [(1, 151936), (4, 151936), (16, 201088), (64, 262144)]
+
+
+def ab_guard(torch, tsv, workloads, dev, reps: int = 7, calls: int = 20) -> dict:
+    """The pull-request page's A/B protocol on MI355X, with the library built
+    with the -inf guard (libtsoftmax.so) and without it
+    (libtsoftmax_noguard.so) in place of the page's main and fix: finite rows
+    (seed B*7+V, logits N(0,1)*4, temperatures U[0.5, 1.5)) on the page's four
+    shapes. It records, per shape, whether every work split gives bitwise the
+    same probabilities in both builds, and the default plan's µs per call in
+    both builds: graph replay of `calls` calls on the same buffers (hot, as the
+    page timed), median of `reps` runs interleaved between the builds."""
+    from temperature_softmax_vocabulary_amd import binding
+    libs = {"guard": binding.lib(), "noguard": binding.load_library(binding.NOGUARD_LIB_PATH)}
+    splits = [(tsv.TS_VARIANT_SPLIT, c) for c in tsv.CHUNKS] + \
+             [(tsv.TS_VARIANT_FUSED, c) for c in tsv.CHUNKS] + [(tsv.TS_VARIANT_ROWWISE, 0)]
+    dp = torch.cuda.get_device_properties(dev)
+    out = {"device": dp.name, "gcn_arch": getattr(dp, "gcnArchName", ""), "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None), "calls_per_replay": calls, "runs": reps,
+           "bitwise_equal": {}, "us_per_call": {}}
+    for B, V in PAGE_SHAPES:
+        w = workloads.make(B, V, "none")
+        x = torch.from_numpy(w.logits).to(dev)
+        t = torch.from_numpy(w.temps).to(dev)
+        key = f"B{B}_V{V}"
+        eq = {}
+        for v, c in splits:
+            ys = {}
+            for name, L in libs.items():
+                y = torch.empty_like(x)
+                st = torch.cuda.current_stream().cuda_stream
+                if L.ts_softmax_variant(x.data_ptr(), t.data_ptr(), None, B, V, y.data_ptr(), v, c, st) != 0:
+                    raise SystemExit(f"{name} build failed on {key} {v}/{c}")
+                ys[name] = y
+            torch.cuda.synchronize()
+            eq[f"{tsv.VARIANT_NAMES[v]}-{c}" if c else tsv.VARIANT_NAMES[v]] = bool(torch.equal(ys["guard"], ys["noguard"]))
+        out["bitwise_equal"][key] = eq
+        graphs = {}
+        for name, L in libs.items():
+            s = torch.cuda.Stream(device=dev)
+            if L.ts_reserve(B, V, s.cuda_stream) != 0:
+                raise SystemExit("ts_reserve failed")
+            y = torch.empty_like(x)
+            with torch.cuda.stream(s):
+                L.ts_softmax(x.data_ptr(), t.data_ptr(), B, V, y.data_ptr(), s.cuda_stream)
+            s.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(calls):
+                    L.ts_softmax(x.data_ptr(), t.data_ptr(), B, V, y.data_ptr(), s.cuda_stream)
+            g.replay()
+            torch.cuda.synchronize()
+            graphs[name] = (g, y)
+        runs = {name: [] for name in libs}
+        for _ in range(reps):
+            for name in libs:
+                g = graphs[name][0]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                runs[name].append(e0.elapsed_time(e1) * 1000.0 / calls)
+        out["us_per_call"][key] = {name: round(statistics.median(r), 3) for name, r in runs.items()}
+        out["us_per_call"][key]["plan"] = list(tsv.ts_plan(B, V))
+        print(f"[ab-guard] {key}: bitwise {sum(eq.values())}/{len(eq)}, us {out['us_per_call'][key]}",
+              file=sys.stderr, flush=True)
+        del graphs
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +422,9 @@ def main(argv=None) -> int:
                     help="side measurements after the timed region: all, only the copy "
                          "(the counter runs' calibration), or none")
     ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
+    ap.add_argument("--ab-guard", action="store_true",
+                    help="instead of the JSON line: the page's A/B (builds with and without the -inf "
+                         "guard: bitwise map over every split, µs per call, median of 7 interleaved)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the JSON line: a table of cold µs per call for every work split "
                          "and chunk size over B in {1..256} x V in {151936, 201088, 262144}")
@@ -401,6 +475,9 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.sweep:
         print(sweep(torch, tsv, workloads, dev, SWEEP_SHAPES, min(args.steps, 200)), flush=True)
+        return 0
+    if args.ab_guard:
+        print(json.dumps(ab_guard(torch, tsv, workloads, dev)), flush=True)
         return 0
     w = workloads.make_config(args.workload)
     B, V = w.B, w.V
