@@ -140,3 +140,54 @@ def test_work_split_table(L, B, V, expect):
     v, c = ctypes.c_int32(), ctypes.c_int32()
     assert L.ts_plan(B, V, ctypes.byref(v), ctypes.byref(c)) == binding.TS_OK
     assert (v.value, c.value) == expect
+
+
+C_PROGRAM = r"""
+#include "tsoftmax.h"
+#include "tsoftmax_measure.h"
+#include <stdio.h>
+
+/* every entry point, taken by address with its declared C type */
+int main(void) {
+    ts_status (*softmax)(const float*, const float*, int64_t, int64_t, float*, hipStream_t) = ts_softmax;
+    ts_status (*masked)(const float*, const float*, const uint32_t*, int64_t, int64_t, float*, hipStream_t) =
+        ts_softmax_masked;
+    ts_status (*variant)(const float*, const float*, const uint32_t*, int64_t, int64_t, float*, int32_t, int32_t,
+                         hipStream_t) = ts_softmax_variant;
+    ts_status (*plan)(int64_t, int64_t, int32_t*, int32_t*) = ts_plan;
+    ts_status (*sample)(const float*, const float*, int64_t, int64_t, int64_t, int32_t*, hipStream_t) = ts_sample;
+    ts_status (*fused)(const float*, const float*, const uint32_t*, const float*, int64_t, int64_t, int64_t, float*,
+                       int32_t*, hipStream_t) = ts_softmax_sample;
+    ts_status (*reserve)(int64_t, int64_t, hipStream_t) = ts_reserve;
+    ts_status (*errors)(hipStream_t, uint32_t*) = ts_device_errors;
+    const char* (*text)(ts_status) = ts_status_string;
+    int32_t (*version)(void) = ts_abi_version;
+    ts_status (*copy)(const float*, float*, int64_t, hipStream_t) = ts_copy_f32;
+    ts_status (*spin)(uint32_t) = ts_debug_set_spin_limit;
+    void* all[] = {(void*)softmax, (void*)masked, (void*)variant, (void*)plan, (void*)sample, (void*)fused,
+                   (void*)reserve, (void*)errors, (void*)text, (void*)version, (void*)copy, (void*)spin};
+    printf("%d %d\n", (int)(sizeof all / sizeof all[0]), TSOFTMAX_ABI_VERSION);
+    return 0;
+}
+"""
+
+
+def test_headers_are_c_and_link_against_the_library(tmp_path):
+    # The boundary is a C ABI: the public headers compile as C11 (no C++), and a
+    # C program that takes every entry point links against libtsoftmax.so. It is
+    # compiled and linked only: nothing runs on a GPU here.
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail(f"{binding.LIB_PATH} missing")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{os.path.join(rocm, 'include')}",
+           str(src), "-o", str(tmp_path / "abi"), binding.LIB_PATH, f"-Wl,-rpath,{os.path.dirname(binding.LIB_PATH)}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
