@@ -8,6 +8,7 @@ the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -98,13 +99,32 @@ def _check(status: int) -> None:
     raise TsError(status, msg)
 
 
+# torch's raw current-stream and current-device accessors: the same values as
+# torch.cuda.current_stream(...).cuda_stream and torch.cuda.current_device(),
+# without building Python stream objects (1.9 and 0.3 us a call otherwise).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_raw_device = getattr(torch._C, "_cuda_getDevice", None)
+_NO_SWITCH = contextlib.nullcontext()
+
+
 def _stream_handle(device: torch.device, stream=None) -> int:
     if stream is None:
+        if _raw_stream is not None:
+            return int(_raw_stream(device.index if device.index is not None else torch.cuda.current_device()))
         stream = torch.cuda.current_stream(device)
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on(device: torch.device):
+    """Make `device` the current HIP device for the call (the library keys its
+    workspace by the current device); no switch when it already is."""
+    cur = _raw_device() if _raw_device is not None else torch.cuda.current_device()
+    return _NO_SWITCH if device.index is None or device.index == cur else torch.cuda.device(device)
+
+
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if isinstance(t, torch.Tensor) and t.is_cuda and t.dtype is dtype and t.dim() == ndim and t.is_contiguous():
+        return
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -113,8 +133,7 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous")
 
 
 def _softmax_args(logits, temps, out):
@@ -136,7 +155,7 @@ def ts_softmax(logits: torch.Tensor, temps: torch.Tensor, out: Optional[torch.Te
                stream=None) -> torch.Tensor:
     """probs = softmax(logits[b, :] / temps[b]) on the device (out may be logits)."""
     B, V, out = _softmax_args(logits, temps, out)
-    with torch.cuda.device(logits.device):
+    with _on(logits.device):
         _check(lib().ts_softmax(logits.data_ptr(), temps.data_ptr(), B, V, out.data_ptr(),
                                 _stream_handle(logits.device, stream)))
     return out
@@ -156,7 +175,7 @@ def ts_softmax_masked(logits: torch.Tensor, temps: torch.Tensor, allowed: torch.
     """ts_softmax with an allowed-id bitmask ([B, ceil(V/32)] int32/uint32; bit j%32
     of word j//32 set = id j allowed) applied as -inf while the logits are read."""
     B, V, out = _softmax_args(logits, temps, out)
-    with torch.cuda.device(logits.device):
+    with _on(logits.device):
         _check(lib().ts_softmax_masked(logits.data_ptr(), temps.data_ptr(), _allowed_arg(allowed, B, V, logits.device),
                                        B, V, out.data_ptr(), _stream_handle(logits.device, stream)))
     return out
@@ -167,7 +186,7 @@ def ts_softmax_variant(logits: torch.Tensor, temps: torch.Tensor, variant: int, 
                        allowed: Optional[torch.Tensor] = None) -> torch.Tensor:
     """ts_softmax (or ts_softmax_masked) with the work split forced (tests and tuning)."""
     B, V, out = _softmax_args(logits, temps, out)
-    with torch.cuda.device(logits.device):
+    with _on(logits.device):
         _check(lib().ts_softmax_variant(logits.data_ptr(), temps.data_ptr(), _allowed_arg(allowed, B, V, logits.device),
                                         B, V, out.data_ptr(), int(variant), int(chunk),
                                         _stream_handle(logits.device, stream)))
@@ -178,7 +197,7 @@ def ts_plan(B: int, V: int, device=None) -> Tuple[int, int]:
     """(variant, chunk) the library picks for (B, V) on `device` (host only)."""
     v, c = ctypes.c_int32(), ctypes.c_int32()
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib().ts_plan(int(B), int(V), ctypes.byref(v), ctypes.byref(c)))
     return v.value, c.value
 
@@ -198,7 +217,7 @@ def ts_sample(probs: torch.Tensor, uniforms: torch.Tensor, out_ids: Optional[tor
         _need(out_ids, "out_ids", torch.int32, 2)
         if tuple(out_ids.shape) != (B, K) or out_ids.device != probs.device:
             raise ValueError("out_ids must be [B, K] int32 on the probs' device")
-    with torch.cuda.device(probs.device):
+    with _on(probs.device):
         _check(lib().ts_sample(probs.data_ptr(), uniforms.data_ptr(), B, V, K, out_ids.data_ptr(),
                                _stream_handle(probs.device, stream)))
     return out_ids
@@ -229,7 +248,7 @@ def ts_softmax_sample(logits: torch.Tensor, temps: torch.Tensor, uniforms: torch
         probs = None
     else:
         _, _, probs = _softmax_args(logits, temps, probs_out)
-    with torch.cuda.device(logits.device):
+    with _on(logits.device):
         _check(lib().ts_softmax_sample(logits.data_ptr(), temps.data_ptr(), _allowed_arg(allowed, B, V, logits.device),
                                        uniforms.data_ptr(), B, V, K,
                                        probs.data_ptr() if probs is not None else None, out_ids.data_ptr(),
@@ -240,7 +259,7 @@ def ts_softmax_sample(logits: torch.Tensor, temps: torch.Tensor, uniforms: torch
 def ts_reserve(max_B: int, max_V: int, device=None, stream=None) -> None:
     """Pre-allocate the workspace of `stream` (default: current) for B <= max_B, V <= max_V."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib().ts_reserve(int(max_B), int(max_V), _stream_handle(dev, stream)))
 
 
@@ -250,7 +269,7 @@ def ts_device_errors(device=None, stream=None) -> int:
     Raises TsError(TS_ERR_SYNC_TIMEOUT) when a fused wait ran out."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     flags = ctypes.c_uint32()
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().ts_device_errors(_stream_handle(dev, stream), ctypes.byref(flags))
     if st not in (TS_OK,):
         _check(st)
@@ -262,7 +281,7 @@ def ts_copy_f32(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tens
     if src.dtype != torch.float32 or dst.dtype != torch.float32 or not src.is_contiguous() \
             or not dst.is_contiguous() or src.numel() != dst.numel() or src.device != dst.device:
         raise ValueError("src and dst must be contiguous float32 tensors of equal size on one device")
-    with torch.cuda.device(src.device):
+    with _on(src.device):
         _check(lib().ts_copy_f32(src.data_ptr(), dst.data_ptr(), src.numel(),
                                  _stream_handle(src.device, stream)))
     return dst
