@@ -145,25 +145,33 @@ __device__ __forceinline__ void apply_allowed(const uint32_t* __restrict__ mrow,
         if (!((bits >> e) & 1u)) v[e] = kNegInf;
 }
 
-// The mask words of a whole chunk, two per lane. Lane t = 64 w + l of the
-// workgroup needs, for group j, word (j NT + t) / 8 = j NT/8 + 8 w + l/8 of the
-// chunk's words: per wave, 8 consecutive words per group. Lane l keeps the
-// words of groups 2 (l / 8) and 2 (l / 8) + 1 at index l % 8, so a group's word
-// is always in the same register of another lane of the same wave, fetched by
-// one cross-lane read (ds_bpermute) when the mask is applied. The loads carry
-// no branch (the index is clamped to the row's last word), so they stay in
-// flight with the data loads until the values are used.
+// The mask words of a whole chunk. Lane t = 64 w + l of the workgroup needs,
+// for group j, word (j NT + t) / 8 = j NT/8 + 8 w + l/8 of the chunk's words:
+// per wave, 8 consecutive words per group. With at most 8 groups, lane l loads
+// the word of group l / 8 at index l % 8 (one word per lane covers every group
+// of the wave); with up to 16, the words of groups 2 (l / 8) and 2 (l / 8) + 1.
+// A group's word is thus always in the same register of another lane of the
+// same wave, fetched by one cross-lane read (ds_bpermute) when the mask is
+// applied. The loads carry no branch (the index is clamped to the row's last
+// word), so they stay in flight with the data loads until the values are used.
+template <int F>
+constexpr int kMaskWordsPerLane = F <= 8 ? 1 : 2;
+
 template <int NT, int F>
 __device__ __forceinline__ void load_mask_words(const uint32_t* __restrict__ mrow, int64_t c0, int64_t V,
                                                 uint32_t (&mw)[2]) {
     static_assert(F <= 16, "two words per lane cover at most 16 groups");
+    constexpr int MW = kMaskWordsPerLane<F>;
     const int l = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     // a uniform base and 32-bit lane offsets (a row has at most 2^26 words)
     const uint32_t* __restrict__ base = mrow + (c0 >> 5);
     const uint32_t last = static_cast<uint32_t>(((V - 1) >> 5) - (c0 >> 5));
+    mw[1] = 0u;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int j = 2 * (l >> 3) + h;
+    for (int h = 0; h < MW; ++h) {
+        // (with fewer than 8 groups, the lanes past them repeat the last group's
+        // words, so they add no memory requests)
+        const int j = MW == 1 ? ((l >> 3) < F ? (l >> 3) : F - 1) : MW * (l >> 3) + h;
         const uint32_t off = static_cast<uint32_t>(j * (NT / 8) + 8 * w + (l & 7));
         mw[h] = base[off < last ? off : last];
     }
@@ -174,10 +182,12 @@ __device__ __forceinline__ void load_mask_words(const uint32_t* __restrict__ mro
 template <int NT, int F>
 __device__ __forceinline__ void apply_mask_words(int64_t c0, int64_t V, const uint32_t (&mw)[2],
                                                  float (&x)[4 * F]) {
+    constexpr int MW = kMaskWordsPerLane<F>;
     const int t = threadIdx.x, l = t & (kWave - 1);
 #pragma unroll
     for (int j = 0; j < F; ++j) {
-        const uint32_t word = static_cast<uint32_t>(__shfl(static_cast<int>(mw[j & 1]), (j >> 1) * 8 + (l >> 3), kWave));
+        const uint32_t word = static_cast<uint32_t>(
+            __shfl(static_cast<int>(mw[j % MW]), (j / MW) * 8 + (l >> 3), kWave));
         const int64_t col = c0 + (static_cast<int64_t>(j) * NT + t) * 4;
         const uint32_t bits = (col < V) ? (word >> (col & 31)) : 0xFu;
 #pragma unroll
