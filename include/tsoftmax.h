@@ -135,8 +135,12 @@ ts_status ts_softmax_variant(const float* logits, const float* temps, const uint
 
 /*
  * The work split ts_softmax would use for (B, V) on the current device, for a
- * 16-byte aligned call with V % 4 == 0. Host only: launches nothing.
+ * 16-byte aligned call with V % 4 == 0. Host only: launches nothing. A row
+ * takes the fused split only if the device holds all of its chunks at once;
+ * with no HIP device present, that check is skipped (the table alone).
  * variant, chunk : host pointers, written on TS_OK.
+ * Errors : TS_ERR_INVALID_ARGUMENT as for ts_softmax, TS_ERR_HIP if the
+ *          occupancy query fails.
  */
 ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
 

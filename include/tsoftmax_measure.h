@@ -33,6 +33,20 @@ ts_status ts_copy_f32(const float* src, float* dst, int64_t n, hipStream_t strea
  */
 ts_status ts_debug_set_spin_limit(uint32_t polls);
 
+/*
+ * Make the planner count on at most `workgroups` co-resident workgroups of a
+ * fused kernel per device, as on a device with fewer compute units (e.g. one
+ * partition of a partitioned GPU). 0 restores the queried capacity. It never
+ * raises the capacity, so every fused grid still fits the device at once.
+ * With a bound below a row's chunk count the default plan takes a larger
+ * chunk or the split pair (ts_plan reports it) and a forced FUSED split
+ * returns TS_ERR_INVALID_ARGUMENT; with one between them, each workgroup
+ * loops over more (row, chunk) items. Takes effect for calls made after it,
+ * on every device. For tests only.
+ * Errors: TS_ERR_INVALID_ARGUMENT for workgroups < 0.
+ */
+ts_status ts_debug_set_resident_cap(int64_t workgroups);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     lib,
     ts_abi_version,
     ts_copy_f32,
+    ts_debug_set_resident_cap,
     ts_debug_set_spin_limit,
     ts_device_errors,
     ts_plan,

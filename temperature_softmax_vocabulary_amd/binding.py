@@ -51,6 +51,7 @@ SIGNATURES = {
     "ts_abi_version": (ctypes.c_int32, []),
     "ts_copy_f32": (ctypes.c_int, [_P, _P, _I64, _P]),
     "ts_debug_set_spin_limit": (ctypes.c_int, [_U32]),
+    "ts_debug_set_resident_cap": (ctypes.c_int, [_I64]),
 }
 
 _lib = None
@@ -290,3 +291,8 @@ def ts_copy_f32(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tens
 def ts_debug_set_spin_limit(polls: int) -> None:
     """Bound (in polls) on a fused kernel's wait; 0 restores the default."""
     _check(lib().ts_debug_set_spin_limit(int(polls)))
+
+
+def ts_debug_set_resident_cap(workgroups: int) -> None:
+    """Bound on the co-resident fused workgroups the planner counts on; 0 removes it."""
+    _check(lib().ts_debug_set_resident_cap(int(workgroups)))

@@ -23,6 +23,8 @@ namespace {
 
 constexpr uint32_t kDefaultSpinLimit = 1u << 18;
 std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
+// Upper bound on the co-resident workgroups the planner counts on (0: none).
+std::atomic<int64_t> g_cap_limit{0};
 
 // ----------------------------------------------------------------------------
 // argument checks (host only: no device reads)
@@ -162,6 +164,26 @@ ts_status resident_cap(int kind, int F, bool vec, int64_t* cap) {
         it = cache.emplace(key, c).first;
     }
     *cap = it->second;
+    const int64_t lim = g_cap_limit.load(std::memory_order_relaxed);
+    if (lim > 0 && *cap > lim) *cap = lim;
+    return TS_OK;
+}
+
+// A fused split needs every chunk of a row resident at once (ts_exchange.h),
+// so rows of more chunks than the row's slots or than the device holds at
+// once cannot take it. Without `on_device` only the slots are checked.
+ts_status fused_fits(int F, bool vec, int64_t V, bool on_device, bool* fits) {
+    *fits = false;
+    const int64_t nch = cdiv(V, 1024 * F);
+    if (nch > tsk::kSlotStride) return TS_OK;
+    if (!on_device) {
+        *fits = true;
+        return TS_OK;
+    }
+    int64_t cap = 0;
+    const ts_status st = resident_cap(tsk::kFusedProbs, F, vec, &cap);
+    if (st != TS_OK) return st;
+    *fits = nch <= cap;
     return TS_OK;
 }
 
@@ -176,25 +198,22 @@ ts_status resident_cap(int kind, int F, bool vec, int64_t* cap) {
 //    better than two of 16384 columns, and a short last chunk wastes less:
 //    at B=64 it is 22.7 against 23.2 us for V=262144 and 14.7 against 17.6 us
 //    for V=151936);
-//  - rows of more than kSlotStride such chunks: fused at 16384 columns while
-//    that fits, else the split pair.
-ts_status choose_plan(int64_t B, int64_t V, bool vec, Plan* p) {
-    (void)vec;
+//  - rows of more chunks than the fused split can hold (kSlotStride, or
+//    what the device holds at once): the next larger chunk while that fits,
+//    else the split pair, which never waits.
+ts_status choose_plan(int64_t B, int64_t V, bool vec, bool on_device, Plan* p) {
     if (V <= tsk::kRowwiseResidentMaxV) {
         *p = Plan{TS_VARIANT_ROWWISE, 0};
         return TS_OK;
     }
-    if (B * V <= (int64_t(1) << 21) && cdiv(V, 4096) <= tsk::kSlotStride) {
-        *p = Plan{TS_VARIANT_FUSED, 4};
-        return TS_OK;
-    }
-    if (cdiv(V, 8192) <= tsk::kSlotStride) {
-        *p = Plan{TS_VARIANT_FUSED, 8};
-        return TS_OK;
-    }
-    if (cdiv(V, 16384) <= tsk::kSlotStride) {
-        *p = Plan{TS_VARIANT_FUSED, 16};
-        return TS_OK;
+    for (int F = B * V <= (int64_t(1) << 21) ? 4 : 8; F <= 16; F *= 2) {
+        bool fits = false;
+        const ts_status st = fused_fits(F, vec, V, on_device, &fits);
+        if (st != TS_OK) return st;
+        if (fits) {
+            *p = Plan{TS_VARIANT_FUSED, F};
+            return TS_OK;
+        }
     }
     *p = Plan{TS_VARIANT_SPLIT, 16};
     return TS_OK;
@@ -241,7 +260,7 @@ ts_status prepare_softmax(const float* logits, const float* temps, const uint32_
 
     Plan plan{variant, F};
     if (variant == TS_VARIANT_AUTO) {
-        ts_status st = choose_plan(B, V, vec, &plan);
+        ts_status st = choose_plan(B, V, vec, true, &plan);
         if (st != TS_OK) return st;
         if (F != 0 && plan.variant != TS_VARIANT_ROWWISE) plan.F = F;
     }
@@ -400,8 +419,11 @@ TS_API ts_status ts_softmax_variant(const float* logits, const float* temps, con
 
 TS_API ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk) {
     if (!sizes_ok(B, V) || !variant || !chunk) return TS_ERR_INVALID_ARGUMENT;
+    // with no HIP device (host-only use) the table alone: no call can run there
+    int ndev = 0;
+    const bool on_device = hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0;
     Plan p{};
-    ts_status st = choose_plan(B, V, true, &p);
+    ts_status st = choose_plan(B, V, true, on_device, &p);
     if (st != TS_OK) return st;
     *variant = p.variant;
     *chunk = p.F * 1024;
@@ -532,5 +554,11 @@ TS_API ts_status ts_copy_f32(const float* src, float* dst, int64_t n, hipStream_
 
 TS_API ts_status ts_debug_set_spin_limit(uint32_t polls) {
     g_spin_limit.store(polls == 0 ? kDefaultSpinLimit : polls, std::memory_order_relaxed);
+    return TS_OK;
+}
+
+TS_API ts_status ts_debug_set_resident_cap(int64_t workgroups) {
+    if (workgroups < 0) return TS_ERR_INVALID_ARGUMENT;
+    g_cap_limit.store(workgroups, std::memory_order_relaxed);
     return TS_OK;
 }

@@ -164,8 +164,10 @@ int main(void) {
     int32_t (*version)(void) = ts_abi_version;
     ts_status (*copy)(const float*, float*, int64_t, hipStream_t) = ts_copy_f32;
     ts_status (*spin)(uint32_t) = ts_debug_set_spin_limit;
+    ts_status (*cap)(int64_t) = ts_debug_set_resident_cap;
     void* all[] = {(void*)softmax, (void*)masked, (void*)variant, (void*)plan, (void*)sample, (void*)fused,
-                   (void*)reserve, (void*)errors, (void*)text, (void*)version, (void*)copy, (void*)spin};
+                   (void*)reserve, (void*)errors, (void*)text, (void*)version, (void*)copy, (void*)spin,
+                   (void*)cap};
     printf("%d %d\n", (int)(sizeof all / sizeof all[0]), TSOFTMAX_ABI_VERSION);
     return 0;
 }

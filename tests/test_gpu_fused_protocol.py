@@ -15,7 +15,7 @@ import torch
 import temperature_softmax_vocabulary_amd as tsv
 from oracle import softmax_ref
 from temperature_softmax_vocabulary_amd import workloads
-from tests.parity import assert_softmax_matches
+from tests.parity import assert_ids_valid, assert_softmax_matches
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -98,6 +98,46 @@ def test_fused_rejects_rows_with_too_many_chunks():
     y = tsv.ts_softmax(x, t)          # the default plan picks a legal split
     torch.cuda.synchronize()
     assert np.allclose(y.cpu().numpy(), 1.0 / 300000, rtol=1e-6)
+
+
+
+F8, F16 = (tsv.TS_VARIANT_FUSED, 8192), (tsv.TS_VARIANT_FUSED, 16384)
+
+
+@pytest.mark.parametrize("cap,plan", [
+    (0, F8),          # the device's own capacity (1024 workgroups of 8192 columns on MI355X)
+    (48, F8),         # 48 workgroups loop over 2048 items
+    (32, F8),         # exactly one row's 32 chunks resident: the smallest legal grid
+    (31, F16),        # a row of 8192-column chunks no longer fits: 16 chunks of 16384
+    (16, F16),
+    (15, (tsv.TS_VARIANT_SPLIT, 16384)),   # nothing fused fits: the split pair, which never waits
+])
+def test_plan_and_grid_follow_the_resident_capacity(cap, plan):
+    # A device that holds fewer workgroups at once (simulated from the host by
+    # lowering the capacity the planner counts on; the grid still fits the
+    # real device) must never get a fused grid that cannot hold a whole row.
+    w, x, t = _case(64, 262144, 11)
+    u = torch.from_numpy(w.uniforms).to(DEV)
+    try:
+        tsv.ts_debug_set_resident_cap(cap)
+        assert tsv.ts_plan(64, 262144) == plan
+        if 0 < cap < 32:
+            with pytest.raises(ValueError):
+                tsv.ts_softmax_variant(x, t, *F8)
+        y = tsv.ts_softmax(x, t)
+        ids, yp = tsv.ts_softmax_sample(x, t, u, probs_out=True)
+        torch.cuda.synchronize()
+    finally:
+        tsv.ts_debug_set_resident_cap(0)
+    print(f"[gpu] resident cap {cap}: plan {plan}", flush=True)
+    # the per-item arithmetic does not depend on the grid: bitwise the same as
+    # the same split on the full device
+    assert torch.equal(y, tsv.ts_softmax_variant(x, t, *plan))
+    ref = softmax_ref(w.logits, w.temps)
+    assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, ref, what=f"cap {cap}")
+    assert_softmax_matches(yp.cpu().numpy(), w.logits, w.temps, ref, what=f"cap {cap} with draw")
+    assert_ids_valid(ids.cpu().numpy(), yp.cpu().numpy(), w.uniforms, what=f"cap {cap}")
+    assert tsv.ts_device_errors() == 0
 
 
 def test_concurrent_full_grids_on_two_streams():
