@@ -612,8 +612,14 @@ def main(argv=None) -> int:
         # every workload, graph replay (the small ones are launch-bound)
         extras["configs_graph_us_per_call"] = configs_graph_us(torch, tsv, workloads, dev)
         dp = torch.cuda.get_device_properties(dev)
+        clock_khz, bus_bits = tsv.ts_device_memory_params(dev)
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
-                            "gcn_arch": getattr(dp, "gcnArchName", "")}
+                            "gcn_arch": getattr(dp, "gcnArchName", ""),
+                            # the peak recomputed from what HIP reports. HBM3E pins move
+                            # 4 bits per reported memory clock (8 Gb/s at 2 GHz); 2 would
+                            # put the peak below the rate the kernels sustain
+                            "mem_clock_khz": clock_khz, "mem_bus_bits": bus_bits,
+                            "hbm_peak_from_props_GBps": round(clock_khz * 1e3 * 4 * bus_bits / 8 / 1e9, 1)}
     if extras:
         extras["kernel_source_sha256"] = kernel_source_hash(ktag)
         result["extras"] = extras

@@ -25,6 +25,17 @@ extern "C" {
 ts_status ts_copy_f32(const float* src, float* dst, int64_t n, hipStream_t stream);
 
 /*
+ * The memory clock (kHz) and memory bus width (bits) that HIP reports for
+ * `device`, from which a peak HBM bandwidth can be recomputed beside the
+ * nominal one: clock x transfers per pin per clock x width / 8 bytes, where
+ * the transfers per clock depend on the memory type (4 for HBM3E).
+ * Host only: launches nothing.
+ * Errors: TS_ERR_INVALID_ARGUMENT for NULL pointers, TS_ERR_HIP if the query
+ * fails (e.g. no such device).
+ */
+ts_status ts_device_memory_params(int32_t device, int32_t* clock_khz, int32_t* bus_bits);
+
+/*
  * Number of polls (each a short sleep plus one load) a fused-kernel
  * workgroup makes while waiting for the rest of its row before it gives up,
  * raises bit 0 of the device error flags and carries on. 0 restores the

@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     ts_debug_set_resident_cap,
     ts_debug_set_spin_limit,
     ts_device_errors,
+    ts_device_memory_params,
     ts_plan,
     ts_reserve,
     ts_sample,

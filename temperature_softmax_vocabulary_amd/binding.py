@@ -52,6 +52,7 @@ SIGNATURES = {
     "ts_copy_f32": (ctypes.c_int, [_P, _P, _I64, _P]),
     "ts_debug_set_spin_limit": (ctypes.c_int, [_U32]),
     "ts_debug_set_resident_cap": (ctypes.c_int, [_I64]),
+    "ts_device_memory_params": (ctypes.c_int, [_I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
 }
 
 _lib = None
@@ -291,6 +292,14 @@ def ts_copy_f32(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tens
 def ts_debug_set_spin_limit(polls: int) -> None:
     """Bound (in polls) on a fused kernel's wait; 0 restores the default."""
     _check(lib().ts_debug_set_spin_limit(int(polls)))
+
+
+def ts_device_memory_params(device=None) -> Tuple[int, int]:
+    """(memory clock in kHz, memory bus width in bits) that HIP reports for `device`."""
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index or 0
+    c, w = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ts_device_memory_params(int(idx), ctypes.byref(c), ctypes.byref(w)))
+    return c.value, w.value
 
 
 def ts_debug_set_resident_cap(workgroups: int) -> None:

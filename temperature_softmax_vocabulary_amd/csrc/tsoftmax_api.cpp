@@ -557,6 +557,16 @@ TS_API ts_status ts_debug_set_spin_limit(uint32_t polls) {
     return TS_OK;
 }
 
+TS_API ts_status ts_device_memory_params(int32_t device, int32_t* clock_khz, int32_t* bus_bits) {
+    if (!clock_khz || !bus_bits) return TS_ERR_INVALID_ARGUMENT;
+    int c = 0, w = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMemoryClockRate, device) != hipSuccess) return TS_ERR_HIP;
+    if (hipDeviceGetAttribute(&w, hipDeviceAttributeMemoryBusWidth, device) != hipSuccess) return TS_ERR_HIP;
+    *clock_khz = c;
+    *bus_bits = w;
+    return TS_OK;
+}
+
 TS_API ts_status ts_debug_set_resident_cap(int64_t workgroups) {
     if (workgroups < 0) return TS_ERR_INVALID_ARGUMENT;
     g_cap_limit.store(workgroups, std::memory_order_relaxed);

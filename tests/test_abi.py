@@ -165,9 +165,10 @@ int main(void) {
     ts_status (*copy)(const float*, float*, int64_t, hipStream_t) = ts_copy_f32;
     ts_status (*spin)(uint32_t) = ts_debug_set_spin_limit;
     ts_status (*cap)(int64_t) = ts_debug_set_resident_cap;
+    ts_status (*mem)(int32_t, int32_t*, int32_t*) = ts_device_memory_params;
     void* all[] = {(void*)softmax, (void*)masked, (void*)variant, (void*)plan, (void*)sample, (void*)fused,
                    (void*)reserve, (void*)errors, (void*)text, (void*)version, (void*)copy, (void*)spin,
-                   (void*)cap};
+                   (void*)cap, (void*)mem};
     printf("%d %d\n", (int)(sizeof all / sizeof all[0]), TSOFTMAX_ABI_VERSION);
     return 0;
 }

@@ -262,3 +262,20 @@ def test_extreme_temperatures():
         for r in (0, 1, 2):
             assert y[r].max() == 1.0 and np.count_nonzero(y[r]) == 1, (v, c, r)
     _no_device_errors()
+
+
+@pytest.mark.parametrize("n,offset", [(1 << 20, 0), ((1 << 20) + 3, 0), (4099, 1), (1, 0)])
+def test_measurement_copy_is_exact(n, offset):
+    # the same-bytes copy is the bandwidth ceiling and the counter calibration:
+    # it must move exactly n floats, aligned or not, and nothing past them
+    src = torch.randn(n + 8, device=DEV)
+    dst = torch.full((n + 8,), 7.0, device=DEV)
+    tsv.ts_copy_f32(src[offset: offset + n], dst[offset: offset + n])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[offset: offset + n], src[offset: offset + n])
+    assert torch.all(dst[:offset] == 7.0) and torch.all(dst[offset + n:] == 7.0)
+
+
+def test_memory_params_for_the_recomputed_peak():
+    clock_khz, bus_bits = tsv.ts_device_memory_params(DEV)
+    assert clock_khz > 0 and bus_bits > 0
