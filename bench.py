@@ -281,6 +281,17 @@ def _oracle_rate(w, target_s: float, threads: int):
     return bytes_per_call * reps / el / 1e9, reps, el
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, target_s: float):
     """The float64 oracle, as it stands, on the host over the same workload:
     first on one thread, then on every host core the process may use (rows
@@ -288,7 +299,12 @@ def cpu_baseline(w, target_s: float):
     g1, r1, e1 = _oracle_rate(w, target_s / 2, 1)
     n = _host_threads()
     gn, rn, en = _oracle_rate(w, target_s / 2, n) if n > 1 else (g1, r1, e1)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
     return {"value": round(gn, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "cpu_model": _cpu_model(), "affinity_cores": affinity,
             "sample": f"full {w.name} workload (B={w.B}, V={w.V}), numpy float64; "
                       f"{n} threads over row blocks: {rn} calls in {en:.1f} s, us/call {en / rn * 1e6:.0f}; "
                       f"one thread: {r1} calls in {e1:.1f} s, {g1:.3f} GB/s, us/call {e1 / r1 * 1e6:.0f}"}
