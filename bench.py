@@ -201,40 +201,68 @@ def _elapsed_us(torch, fn, n):
     return e0.elapsed_time(e1) * 1000.0 / n
 
 
-def configs_graph_us(torch, tsv, workloads, dev) -> dict:
-    """µs per ts_softmax call for each of the five workloads, cold, from graph
-    replay (launch gaps removed): rotating slices of one >= 512 MiB buffer
-    pair, all captured into one graph."""
-    res = {}
-    for name in workloads.CONFIG_ORDER:
-        w = workloads.make_config(name)
-        B, V = w.B, w.V
-        nsets = min(512, max(2, math.ceil((512 << 20) / (2 * B * V * 4))))
-        x = torch.from_numpy(w.logits).to(dev).unsqueeze(0).repeat(nsets, 1, 1)
-        t = torch.from_numpy(w.temps).to(dev)
-        y = torch.empty_like(x)
-        s = torch.cuda.Stream(device=dev)
-        tsv.ts_reserve(B, V, device=dev, stream=s)
-        with torch.cuda.stream(s):
-            for i in range(nsets):
+def graph_cold_us(torch, tsv, dev, w, op: str = "softmax") -> float:
+    """µs per call of ts_softmax (op="softmax") or of the same-bytes copy
+    (op="copy") on workload w, cold, from graph replay (launch gaps removed):
+    rotating slices of one >= 512 MiB buffer pair, all captured into one
+    graph."""
+    B, V = w.B, w.V
+    nsets = min(512, max(2, math.ceil((512 << 20) / (2 * B * V * 4))))
+    x = torch.from_numpy(w.logits).to(dev).unsqueeze(0).repeat(nsets, 1, 1)
+    t = torch.from_numpy(w.temps).to(dev)
+    y = torch.empty_like(x)
+    s = torch.cuda.Stream(device=dev)
+    tsv.ts_reserve(B, V, device=dev, stream=s)
+
+    def calls():
+        for i in range(nsets):
+            if op == "copy":
+                tsv.ts_copy_f32(x[i], y[i])
+            else:
                 tsv.ts_softmax(x[i], t, out=y[i])
-        s.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for i in range(nsets):
-                tsv.ts_softmax(x[i], t, out=y[i])
+    with torch.cuda.stream(s):
+        calls()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
         g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 5
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = round(e0.elapsed_time(e1) * 1000.0 / (reps * nsets), 3)
-        del x, y, g
-    return res
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * nsets)
+    del x, y, g
+    return round(us, 3)
+
+
+def configs_graph_us(torch, tsv, workloads, dev) -> dict:
+    """µs per ts_softmax call for each of the five workloads, cold, by graph replay."""
+    return {name: graph_cold_us(torch, tsv, dev, workloads.make_config(name)) for name in workloads.CONFIG_ORDER}
+
+
+def shards_table(torch, tsv, workloads, dev, B: int, V: int) -> str:
+    """One GPU's share of a (B, V) softmax split over G GPUs, by batch (B/G
+    rows) and by vocabulary (V/G columns per row), for G in 1, 2, 4, 8: µs per
+    call cold by graph replay, against a copy of the same bytes. The
+    collectives the vocabulary split would add are not part of it."""
+    lines = ["| G | share | B | V | softmax µs | copy µs | softmax / copy | GB/s |", "|---|---|---|---|---|---|---|---|"]
+    for G in (1, 2, 4, 8):
+        for kind, (b, v) in (("batch", (B // G, V)), ("vocabulary", (B, V // G))):
+            if G == 1 and kind == "vocabulary":
+                continue
+            w = workloads.make(b, v, "quarters")
+            sm = graph_cold_us(torch, tsv, dev, w)
+            cp = graph_cold_us(torch, tsv, dev, w, "copy")
+            gbs = 2 * b * v * 4 / sm / 1e3
+            lines.append(f"| {G} | {kind if G > 1 else 'whole'} | {b} | {v} | {sm:.2f} | {cp:.2f} | "
+                         f"{sm / cp:.3f} | {gbs:.0f} |")
+            print(f"[shards] G={G} {kind} B={b} V={v} done", flush=True)
+    return "\n".join(lines)
 
 
 def _host_threads() -> int:
@@ -441,6 +469,8 @@ def main(argv=None) -> int:
     ap.add_argument("--ab-guard", action="store_true",
                     help="instead of the JSON line: the page's A/B (builds with and without the -inf "
                          "guard: bitwise map over every split, µs per call, median of 7 interleaved)")
+    ap.add_argument("--shards", action="store_true",
+                    help="print one GPU's share of the workload split over 2, 4, 8 GPUs (graph replay, cold)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the JSON line: a table of cold µs per call for every work split "
                          "and chunk size over B in {1..256} x V in {151936, 201088, 262144}")
@@ -491,6 +521,10 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.sweep:
         print(sweep(torch, tsv, workloads, dev, SWEEP_SHAPES, min(args.steps, 200)), flush=True)
+        return 0
+    if args.shards:
+        w = workloads.make_config(args.workload)
+        print(shards_table(torch, tsv, workloads, dev, w.B, w.V), flush=True)
         return 0
     if args.ab_guard:
         print(json.dumps(ab_guard(torch, tsv, workloads, dev)), flush=True)
