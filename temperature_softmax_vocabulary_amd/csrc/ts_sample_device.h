@@ -47,23 +47,33 @@ __device__ __forceinline__ uint64_t lane_value_u64(uint64_t v, int src) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Inclusive prefix sum over the lanes of a wave, in lane order.
+// A 64-bit DPP lane move (two 32-bit moves); 0 where the source lane lies
+// outside its row or the row is masked off. All 64 lanes must be active.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64_or0(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, ROW_MASK, 0xF,
+                                               false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, ROW_MASK,
+                                               0xF, false);
+    return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// Inclusive prefix sum over the lanes of a wave, in lane order, with DPP moves
+// only (no LDS): shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the
+// last lane of rows 0 and 2 into rows 1 and 3 (row_bcast15), then lane 31 into
+// rows 2 and 3 (row_bcast31). All 64 lanes must be active.
 __device__ __forceinline__ uint64_t wave_inclusive_scan_u64(uint64_t v) {
-    const int ln = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint64_t y = __shfl_up(v, d, kWave);
-        if (ln >= d) v += y;
-    }
+    v += dpp_u64_or0<0x111>(v);        // row_shr:1
+    v += dpp_u64_or0<0x112>(v);        // row_shr:2
+    v += dpp_u64_or0<0x114>(v);        // row_shr:4
+    v += dpp_u64_or0<0x118>(v);        // row_shr:8
+    v += dpp_u64_or0<0x142, 0xA>(v);   // row_bcast15 -> rows 1, 3
+    v += dpp_u64_or0<0x143, 0xC>(v);   // row_bcast31 -> rows 2, 3
     return v;
 }
 
 // Sum over the 64 lanes of a wave, returned to every lane.
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) { return lane_value_u64(wave_inclusive_scan_u64(v), 63); }
 
 // A group's weight from its probability partials: the four waves' sums, added
 // in one fixed order.
