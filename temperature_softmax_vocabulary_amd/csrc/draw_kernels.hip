@@ -164,76 +164,73 @@ __device__ __forceinline__ uint64_t carry_target(uint64_t T, uint64_t P, uint64_
     return Tc < L ? Tc : L - 1;
 }
 
+// Level 1 of a row, common to all its targets. The row's groups, 64 per tile,
+// lane l holding group b0 + l, get float weights (from logits: pl rescaled to
+// the row's max, as in the finalize, so that a fully masked group weighs
+// exactly 0; from probabilities: the waves' sums), then integers at one
+// power-of-two scale 2^s1.
 template <int KIND>
-__global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
-    const int ln = threadIdx.x & (kWave - 1);
-    const int64_t wid = static_cast<int64_t>(blockIdx.x) * DW + threadIdx.x / kWave;
-    if (wid >= a.B * a.K) return;   // the whole wave
-    const int64_t row = wid / a.K;
-    const int64_t ng = a.ngroups;
-    const float4* grow = a.gpart + row * ng;
-    int32_t* out = a.out_ids + wid;
-    // independent loads first
-    const float u = a.uniforms[wid];
-    const float k = KIND == kDrawLogits ? exp2_scale(a.temps[row]) : 0.0f;
+struct RowGroups {
+    const float4* grow;   // the row's group partials
+    int64_t ng;
+    float k;              // exp2 scale (logits)
+    float gsh;            // the row's guarded max (logits)
+    int s1;
 
-    // level 1: the row's groups, 64 per tile, lane l holding group b0 + l
-    const float4 gv = ln < ng ? grow[ln] : make_float4(kNegInf, 0.0f, 0.0f, 0.0f);
-    float gsh = 0.0f;
-    if constexpr (KIND == kDrawLogits) {
-        float mm = gv.x;
-        for (int64_t b0 = kWave; b0 < ng; b0 += kWave) mm = fmaxf(mm, b0 + ln < ng ? grow[b0 + ln].x : kNegInf);
-        gsh = guarded_shift(wave_reduce<MaxOp>(mm));
-    }
-    auto group_weight = [&](float4 v, int64_t i) -> float {
+    __device__ __forceinline__ float weight(float4 v, int64_t i) const {
         if (i >= ng) return 0.0f;
         if constexpr (KIND == kDrawLogits) return masked_term(v.x, v.y * exp2_hw((v.x - gsh) * k));
         else return group_prob_sum(v);
-    };
-    const float gw0 = group_weight(gv, ln);
-    float tl = gw0;
-    for (int64_t b0 = kWave; b0 < ng; b0 += kWave)
-        tl += b0 + ln < ng ? group_weight(grow[b0 + ln], b0 + ln) : 0.0f;
-    const float tot = wave_reduce<SumOp>(tl);
-    if (!(tot > 0.0f) || !(tot < __builtin_huge_valf())) {   // nothing can be drawn
-        if (ln == 0) *out = -1;
-        return;
     }
-    const int s1 = scale_exponent(tot);
-    const uint64_t q0 = fixed_point(gw0, s1);
-    const uint64_t incl0 = wave_inclusive_scan_u64(q0);
+    __device__ __forceinline__ float4 part(int64_t i) const {
+        return i < ng ? grow[i] : make_float4(kNegInf, 0.0f, 0.0f, 0.0f);
+    }
+    // group b0 + ln's integer weight (0 past the row's end)
+    __device__ __forceinline__ uint64_t q(int64_t b0, int ln) const {
+        return fixed_point(weight(part(b0 + ln), b0 + ln), s1);
+    }
+};
+
+// Fills r for `row` and returns the row's integer total Q, or 0 when nothing
+// can be drawn (no positive weight, or a total that is not finite). q0 and
+// incl0: the first tile's integers and their inclusive scan. Called by all
+// lanes of one wave.
+template <int KIND>
+__device__ __forceinline__ uint64_t row_level1(const DrawArgs& a, int64_t row, float k, int ln, RowGroups<KIND>& r,
+                                               uint64_t& q0, uint64_t& incl0) {
+    r.grow = a.gpart + row * a.ngroups;
+    r.ng = a.ngroups;
+    r.k = k;
+    r.gsh = 0.0f;
+    const float4 gv = r.part(ln);
+    if constexpr (KIND == kDrawLogits) {
+        float mm = gv.x;
+        for (int64_t b0 = kWave; b0 < r.ng; b0 += kWave) mm = fmaxf(mm, r.part(b0 + ln).x);
+        r.gsh = guarded_shift(wave_reduce<MaxOp>(mm));
+    }
+    const float gw0 = r.weight(gv, ln);
+    float tl = gw0;
+    for (int64_t b0 = kWave; b0 < r.ng; b0 += kWave) tl += r.weight(r.part(b0 + ln), b0 + ln);
+    const float tot = wave_reduce<SumOp>(tl);
+    if (!(tot > 0.0f) || !(tot < __builtin_huge_valf())) return 0;
+    r.s1 = scale_exponent(tot);
+    q0 = fixed_point(gw0, r.s1);
+    incl0 = wave_inclusive_scan_u64(q0);
     uint64_t Q = lane_value_u64(incl0, kWave - 1);
-    if (ng > kWave) {   // the row's integer total over every tile
+    if (r.ng > kWave) {   // the row's integer total over every tile
         uint64_t ql = 0;
-        for (int64_t b0 = kWave; b0 < ng; b0 += kWave)
-            ql += b0 + ln < ng ? fixed_point(group_weight(grow[b0 + ln], b0 + ln), s1) : 0;
+        for (int64_t b0 = kWave; b0 < r.ng; b0 += kWave) ql += r.q(b0, ln);
         Q += wave_sum_u64(ql);
     }
-    const uint64_t T = target_of(u, Q);
-    int64_t G = -1;
-    uint64_t PG = 0, qG = 0, carry = 0;
-    for (int64_t b0 = 0; b0 < ng; b0 += kWave) {
-        uint64_t q = q0, incl = incl0;
-        if (b0 > 0) {
-            q = b0 + ln < ng ? fixed_point(group_weight(grow[b0 + ln], b0 + ln), s1) : 0;
-            incl = wave_inclusive_scan_u64(q);
-        }
-        const int src = find_lane(q, incl, carry, T);
-        if (src >= 0) {
-            G = b0 + src;
-            PG = carry + lane_value_u64(incl - q, src);
-            qG = lane_value_u64(q, src);
-            break;
-        }
-        carry += lane_value_u64(incl, kWave - 1);
-    }
-    // (the ranges tile [0, Q) and T < Q, so this and the two checks below
-    // never fire; they keep every index in bounds regardless)
-    if (G < 0) {
-        if (ln == 0) *out = -1;
-        return;
-    }
+    return Q;   // >= 1: the largest group's integer is at least 2^60 / ng
+}
 
+// Levels 2 and 3 of one target, by one wave: the target T lies in
+// [PG, PG + qG) of the level-1 integers, in group G. Writes the id (or -1).
+template <int KIND>
+__device__ __forceinline__ void resolve_in_group(const DrawArgs& a, int64_t row, float k, int64_t G, uint64_t T,
+                                                 uint64_t PG, uint64_t qG, int32_t* out, int ln) {
+    const int64_t ng = a.ngroups;
     // level 2: the group's 64 blocks, lane l holding block l
     // (block weights: sums of the group's exponentials at its max, or of probabilities)
     const float bw = a.bpart[(row * ng + G) * kBlocksPerGroup + ln].x;
@@ -242,6 +239,8 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     const uint64_t incl2 = wave_inclusive_scan_u64(qb);
     const uint64_t T2 = carry_target(T, PG, qG, lane_value_u64(incl2, kWave - 1));
     const int b = find_lane(qb, incl2, 0, T2);
+    // (the ranges tile each level's total and the target lies below it, so
+    // this and the check below never fire; they keep every index in bounds)
     if (b < 0) {
         if (ln == 0) *out = -1;
         return;
@@ -258,7 +257,7 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
         if (const uint32_t* mrow = draw_mask_row(a, row)) {
             if (col < a.V && !((mrow[col >> 5] >> (col & 31)) & 1u)) v = kNegInf;
         }
-        v = exp2_hw((v - guarded_shift(grow[G].x)) * k);   // as the partials kernel formed them
+        v = exp2_hw((v - guarded_shift(a.gpart[row * ng + G].x)) * k);   // as the partials kernel formed them
     }
     const int s3 = scale_exponent(bx);   // each entry <= the block's sum
     const uint64_t qe = fixed_point(v, s3);
@@ -267,6 +266,107 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve(DrawArgs a) {
     const int e = find_lane(qe, incl3, 0, T3);
     if (e < 0 && ln == 0) *out = -1;
     if (ln == e) *out = static_cast<int32_t>(col);
+}
+
+// ts_draw_resolve_rows: workgroup (row, tile) draws targets tile TW + w,
+// w < TW, of the row, one wave each. Wave 0 does level 1 once for all of them
+// and leaves the groups' inclusive integer prefix sums in LDS (incl[0, ng),
+// then the row's total Q at incl[ng]); each wave then finds its target's group
+// as the first with a prefix above the target, which is the group whose range
+// holds it. The integers are those of ts_draw_resolve_waves, so are the ids.
+// Dynamic LDS: 8 (ngroups + 1) bytes.
+template <int KIND>
+__global__ __launch_bounds__(kWave * kResolveRowTargets) void ts_draw_resolve_rows(DrawArgs a) {
+    constexpr int TW = kResolveRowTargets;
+    extern __shared__ uint64_t incl[];
+    const int ln = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int64_t ntiles = (a.K + TW - 1) / TW;
+    const int64_t row = blockIdx.x / ntiles;
+    const int64_t kk = (blockIdx.x - row * ntiles) * TW + w;
+    const int64_t ng = a.ngroups;
+    const bool active = kk < a.K;   // wave-uniform
+    const float u = active ? a.uniforms[row * a.K + kk] : 0.0f;
+    const float k = KIND == kDrawLogits ? exp2_scale(a.temps[row]) : 0.0f;
+    if (w == 0) {
+        RowGroups<KIND> r;
+        uint64_t q0 = 0, incl0 = 0;
+        const uint64_t Q = row_level1<KIND>(a, row, k, ln, r, q0, incl0);
+        if (Q > 0) {
+            if (ln < ng) incl[ln] = incl0;
+            uint64_t carry = lane_value_u64(incl0, kWave - 1);
+            for (int64_t b0 = kWave; b0 < ng; b0 += kWave) {
+                const uint64_t t = wave_inclusive_scan_u64(r.q(b0, ln));
+                if (b0 + ln < ng) incl[b0 + ln] = carry + t;
+                carry += lane_value_u64(t, kWave - 1);
+            }
+        }
+        if (ln == 0) incl[ng] = Q;
+    }
+    __syncthreads();
+    if (!active) return;
+    int32_t* out = a.out_ids + row * a.K + kk;
+    const uint64_t Q = incl[ng];
+    if (Q == 0) {   // nothing can be drawn
+        if (ln == 0) *out = -1;
+        return;
+    }
+    const uint64_t T = target_of(u, Q);
+    int64_t G = -1;
+    for (int64_t b0 = 0; b0 < ng && G < 0; b0 += kWave) {
+        const uint64_t hits = __ballot(b0 + ln < ng && incl[b0 + ln] > T);
+        if (hits) G = b0 + __ffsll(static_cast<unsigned long long>(hits)) - 1;
+    }
+    if (G < 0) {   // (never: incl[ng - 1] = Q > T)
+        if (ln == 0) *out = -1;
+        return;
+    }
+    const uint64_t PG = G > 0 ? incl[G - 1] : 0;
+    resolve_in_group<KIND>(a, row, k, G, T, PG, incl[G] - PG, out, ln);
+}
+
+// ts_draw_resolve_waves (rows whose prefix sums do not fit LDS): wave w of the
+// grid draws target w % K of row w / K and does level 1 itself, finding the
+// target's group tile by tile.
+template <int KIND>
+__global__ __launch_bounds__(DT) void ts_draw_resolve_waves(DrawArgs a) {
+    const int ln = threadIdx.x & (kWave - 1);
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * DW + threadIdx.x / kWave;
+    if (wid >= a.B * a.K) return;   // the whole wave
+    const int64_t row = wid / a.K;
+    int32_t* out = a.out_ids + wid;
+    const float u = a.uniforms[wid];
+    const float k = KIND == kDrawLogits ? exp2_scale(a.temps[row]) : 0.0f;
+    RowGroups<KIND> r;
+    uint64_t q0 = 0, incl0 = 0;
+    const uint64_t Q = row_level1<KIND>(a, row, k, ln, r, q0, incl0);
+    if (Q == 0) {   // nothing can be drawn
+        if (ln == 0) *out = -1;
+        return;
+    }
+    const uint64_t T = target_of(u, Q);
+    int64_t G = -1;
+    uint64_t PG = 0, qG = 0, carry = 0;
+    for (int64_t b0 = 0; b0 < r.ng; b0 += kWave) {
+        uint64_t q = q0, incl = incl0;
+        if (b0 > 0) {
+            q = r.q(b0, ln);
+            incl = wave_inclusive_scan_u64(q);
+        }
+        const int src = find_lane(q, incl, carry, T);
+        if (src >= 0) {
+            G = b0 + src;
+            PG = carry + lane_value_u64(incl - q, src);
+            qG = lane_value_u64(q, src);
+            break;
+        }
+        carry += lane_value_u64(incl, kWave - 1);
+    }
+    if (G < 0) {   // (never: the ranges tile [0, Q) and T < Q)
+        if (ln == 0) *out = -1;
+        return;
+    }
+    resolve_in_group<KIND>(a, row, k, G, T, PG, qG, out, ln);
 }
 
 // Groups per workgroup of the partials kernel: two (32 KiB of reads) once the
@@ -300,12 +400,34 @@ hipError_t launch_draw_partials(const DrawArgs& a, int ld, int kind, hipStream_t
     return wide ? partials_ld<kPartialsGPW>(a, ld, kind, s) : partials_ld<1>(a, ld, kind, s);
 }
 
-hipError_t launch_draw_resolve(const DrawArgs& a, int kind, hipStream_t s) {
-    const int64_t waves = a.B * a.K;
-    const dim3 grid(static_cast<uint32_t>((waves + DW - 1) / DW));
-    if (kind == kDrawLogits) hipLaunchKernelGGL((ts_draw_resolve<kDrawLogits>), grid, dim3(DT), 0, s, a);
-    else hipLaunchKernelGGL((ts_draw_resolve<kDrawProbs>), grid, dim3(DT), 0, s, a);
+namespace {
+
+template <int KIND>
+hipError_t resolve_impl(const DrawArgs& a, hipStream_t s) {
+    if (resolve_shares_rows(a.B, a.K, a.ngroups, a.cus)) {
+        const dim3 grid(static_cast<uint32_t>(a.B * ((a.K + kResolveRowTargets - 1) / kResolveRowTargets)));
+        const size_t lds = static_cast<size_t>(a.ngroups + 1) * sizeof(uint64_t);
+        hipLaunchKernelGGL((ts_draw_resolve_rows<KIND>), grid, dim3(kWave * kResolveRowTargets), lds, s, a);
+    } else {
+        const dim3 grid(static_cast<uint32_t>((a.B * a.K + DW - 1) / DW));
+        hipLaunchKernelGGL((ts_draw_resolve_waves<KIND>), grid, dim3(DT), 0, s, a);
+    }
     return hipGetLastError();
+}
+
+}  // namespace
+
+// Sharing level 1 saves each row's redundant level-1 work but puts 16 targets
+// on one compute unit; measured on MI355X at B=64 (µs per ts_sample call,
+// cold), it wins once the grid still gives every compute unit a workgroup:
+// K=16 +1.0, K=32 +0.7, K=64 -0.3, K=128 -0.6, K=256 -0.9.
+bool resolve_shares_rows(int64_t B, int64_t K, int64_t ngroups, int64_t cus) {
+    if ((ngroups + 1) * static_cast<int64_t>(sizeof(uint64_t)) > kResolveLdsMax) return false;
+    return K >= kResolveRowTargets && B * ((K + kResolveRowTargets - 1) / kResolveRowTargets) >= cus;
+}
+
+hipError_t launch_draw_resolve(const DrawArgs& a, int kind, hipStream_t s) {
+    return kind == kDrawLogits ? resolve_impl<kDrawLogits>(a, s) : resolve_impl<kDrawProbs>(a, s);
 }
 
 }  // namespace tsk

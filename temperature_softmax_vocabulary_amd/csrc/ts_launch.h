@@ -85,12 +85,19 @@ struct DrawArgs {
     int64_t V;
     int64_t K;
     int64_t ngroups;          // ceil(V / kDrawGroup)
+    int64_t cus;              // compute units of the device (the resolve's choice of kernel)
 };
 // Group and block partials over the whole of x (one read), one group per
 // workgroup; ld: a kLd* for x's rows.
 hipError_t launch_draw_partials(const DrawArgs& a, int ld, int kind, hipStream_t s);
 // One wave per (row, target): the target's group, then its block, then its id.
+// With resolve_shares_rows, 16 targets of a row share a workgroup, whose
+// first wave computes the row's level 1 once into LDS; otherwise every wave
+// does level 1 itself.
+constexpr int kResolveRowTargets = 16;
+constexpr int64_t kResolveLdsMax = 65536;   // 8 (ngroups + 1) bytes must fit
 hipError_t launch_draw_resolve(const DrawArgs& a, int kind, hipStream_t s);
+bool resolve_shares_rows(int64_t B, int64_t K, int64_t ngroups, int64_t cus);
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, bool vec, hipStream_t s);
 

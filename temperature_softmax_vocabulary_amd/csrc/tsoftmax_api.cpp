@@ -169,6 +169,23 @@ ts_status resident_cap(int kind, int F, bool vec, int64_t* cap) {
     return TS_OK;
 }
 
+// Compute units of the current device (cached per device).
+ts_status device_cus(int64_t* cus) {
+    static std::mutex mu;
+    static std::map<int, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TS_ERR_HIP;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it == cache.end()) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return TS_ERR_HIP;
+        it = cache.emplace(dev, n).first;
+    }
+    *cus = it->second;
+    return TS_OK;
+}
+
 // A fused split needs every chunk of a row resident at once (ts_exchange.h),
 // so rows of more chunks than the row's slots or than the device holds at
 // once cannot take it. Without `on_device` only the slots are checked.
@@ -384,6 +401,8 @@ ts_status launch_draw(int kind, const float* x, const float* temps, const uint32
     d.V = V;
     d.K = K;
     d.ngroups = cdiv(V, tsk::kDrawGroup);
+    ts_status st = device_cus(&d.cus);
+    if (st != TS_OK) return st;
     d.gpart = reinterpret_cast<float4*>(v.part);
     d.bpart = v.part + 2 * B * d.ngroups;
     const int ld = aligned16(x) && (V % 4 == 0) ? tsk::kLdAligned : tsk::kLdUnaligned;
@@ -395,6 +414,7 @@ ts_status launch_draw(int kind, const float* x, const float* temps, const uint32
 }
 
 // Size limits of the draw's grids (32-bit grid dimensions).
+// (the resolve's grid is at most the one-wave-per-target grid)
 bool draw_sizes_ok(int64_t B, int64_t V, int64_t K) {
     return B * cdiv(V, tsk::kDrawGroup) <= INT32_MAX && cdiv(B * K, 4) <= INT32_MAX;
 }

@@ -110,10 +110,11 @@ def test_misaligned_probs_pointer():
     assert_ids_valid(ids, p32, w.uniforms)
 
 
-def test_row_without_mass_gives_minus_one():
+@pytest.mark.parametrize("K", [4, 4100])   # one wave per target; rows sharing level 1 (4100 % 16 = 4)
+def test_row_without_mass_gives_minus_one(K):
     p = np.zeros((2, 1000), np.float32)
     p[1, 10] = 1.0
-    u = np.full((2, 4), 0.5, np.float32)
+    u = np.full((2, K), 0.5, np.float32)
     ids = _sample(p, u)
     assert np.all(ids[0] == -1) and np.all(ids[1] == 10)
 
@@ -127,12 +128,16 @@ def test_unnormalised_weights_scale_by_total():
     assert_ids_valid(ids, p, u)
 
 
-def test_dyadic_rows_exact_across_groups_and_blocks():
+@pytest.mark.parametrize("V,K", [
+    (3 * 4096 + 100, 64),       # one wave per target, each doing level 1
+    (3 * 4096 + 100, 1030),     # 16 targets per workgroup share level 1 (grid >= the CUs; 1030 % 16 = 6)
+    (193 * 4096 - 5, 1030),     # the same over 4 tiles of 64 groups
+])
+def test_dyadic_rows_exact_across_groups_and_blocks(V, K):
     # Weights 2^-e spread over several 4096-id groups and 64-id blocks (some
     # blocks and groups empty): every float sum is exact, so every level of the
     # draw is exact and the ids must equal the oracle's, at and next to every
     # CDF boundary.
-    V = 3 * 4096 + 100
     rng = np.random.default_rng(21)
     B = 4
     p = np.zeros((B, V), np.float32)
@@ -148,7 +153,7 @@ def test_dyadic_rows_exact_across_groups_and_blocks():
         cuts = np.unique(c[r]) / t
         row = np.concatenate([cuts, np.nextafter(cuts.astype(np.float32), np.float32(0)),
                               np.nextafter(cuts.astype(np.float32), np.float32(2)), [0.0, 1.0]])
-        us.append(np.resize(row, 64))
+        us.append(np.resize(row, K))
     u = np.array(us, np.float32)
     ids = _sample(p, u)
     np.testing.assert_array_equal(ids, sample_ref(p, u))
@@ -167,3 +172,36 @@ def test_nan_and_negative_entries_are_never_drawn():
     clean = np.where(p > 0, p, 0).astype(np.float32)
     assert_ids_valid(ids, clean, u, what="nan/negative")
     assert not bad[np.arange(3)[:, None], ids].any()
+
+
+@pytest.mark.parametrize("ng,K", [(8191, 64), (8191, 4096), (8193, 4096)])
+def test_rows_at_the_shared_prefix_limit(ng, K):
+    # With enough targets (here 4096 on one row: 256 workgroups) the resolve
+    # keeps a row's level-1 prefix sums in LDS (8 bytes per 4096-id group,
+    # plus the total) while they fit 64 KiB: 8191 groups just do (128 tiles of
+    # 64 groups); at 8193, and with few targets, every target's wave does
+    # level 1 itself. Dyadic weights in a few groups far apart: ids exact at
+    # and next to every boundary. The same row as logits (-inf elsewhere)
+    # through the ids-only draw: ids valid against the oracle.
+    V = ng * 4096 - 7
+    print(f"[gpu] long row: {ng} groups, V={V}, K={K}", flush=True)
+    rng = np.random.default_rng(ng)
+    cols = np.unique(np.concatenate([rng.choice(V, size=24, replace=False), [0, 4095, 4096, V - 1]]))
+    w = np.float32(2.0) ** -rng.integers(1, 8, size=cols.size).astype(np.float32)
+    p = np.zeros((1, V), np.float32)
+    p[0, cols] = w
+    c = np.cumsum(w.astype(np.float64))
+    cuts = c / c[-1]
+    row = np.concatenate([cuts, np.nextafter(cuts.astype(np.float32), np.float32(0)), [0.0, 1.0]])
+    u = np.resize(row, (1, K)).astype(np.float32)
+    np.testing.assert_array_equal(_sample(p, u), sample_ref(p, u))
+    x = np.full((1, V), -np.inf, np.float32)
+    x[0, cols] = np.log(w)
+    t = np.ones(1, np.float32)
+    ids, _ = tsv.ts_softmax_sample(torch.from_numpy(x).to(DEV), torch.from_numpy(t).to(DEV),
+                                   torch.from_numpy(u).to(DEV))
+    torch.cuda.synchronize()
+    ref = softmax_ref(x, t)
+    assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), u, what=f"{ng} groups, logits")
+    assert np.all(np.isin(ids.cpu().numpy(), cols))
+    assert tsv.ts_device_errors() == 0
