@@ -15,14 +15,17 @@
 //    -inf guard of the fix paragraph; from probabilities, the sum of the
 //    positive entries (one share per wave). Each block gets its sum of the
 //    same terms: the exponentials at its group's max, or the probabilities.
-//  ts_draw_resolve: one wave per (row, target), three levels. At each level
-//    the 64 lanes hold 64 float weights -- the row's groups (for logits, their
-//    pl rescaled to the row's max as in the finalize, so that a fully masked
+//  the resolve: one wave per (row, target), three levels. At each level the
+//    64 lanes hold 64 float weights -- the row's groups (for logits, their pl
+//    rescaled to the row's max as in the finalize, so that a fully masked
 //    group weighs exactly 0), then the chosen group's blocks, then the chosen
 //    block's entries -- which become integers at one power-of-two scale; an
 //    integer prefix sum over the lanes gives each its range, and the lane whose
 //    range holds the target is chosen. The target is carried into the next
 //    level's integer units in double precision and clamped to its total.
+//    Level 1 is the same for all targets of a row: ts_draw_resolve_rows
+//    computes it once per 16 targets and shares it through LDS,
+//    ts_draw_resolve_waves in every wave (resolve_shares_rows picks).
 // Every wave computes the same integers from the same partials, so at each
 // level the ranges tile the total exactly. The draw follows the rule up to the
 // float rounding of the group and block weights (about 1e-7 of the row total);
