@@ -163,9 +163,10 @@ def test_sample_long_rows():
     assert_ids_valid(ids, p, u, what="fallback")
 
 
+@pytest.mark.parametrize("K", [64, 256])   # one wave per target; 16 targets of a row per workgroup
 @pytest.mark.parametrize("with_probs", [True, False], ids=["with_probs", "ids_only"])
-def test_graph_capture_softmax_sample(with_probs):
-    B, V, K = 16, 201088, 64
+def test_graph_capture_softmax_sample(with_probs, K):
+    B, V = 16, 201088
     s = torch.cuda.Stream(device=DEV)
     tsv.ts_reserve(B, V, device=DEV, stream=s)
     x = torch.zeros((B, V), dtype=torch.float32, device=DEV)
