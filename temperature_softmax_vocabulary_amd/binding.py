@@ -166,7 +166,7 @@ def ts_softmax(logits: torch.Tensor, temps: torch.Tensor, out: Optional[torch.Te
 def _allowed_arg(allowed, B, V, device):
     if allowed is None:
         return None
-    _need(allowed, "allowed", torch.int32 if allowed.dtype == torch.int32 else torch.uint32, 2)
+    _need(allowed, "allowed", torch.int32 if getattr(allowed, "dtype", None) == torch.int32 else torch.uint32, 2)
     if tuple(allowed.shape) != (B, (V + 31) // 32) or allowed.device != device:
         raise ValueError(f"allowed must be [B, ceil(V/32)] = [{B}, {(V + 31) // 32}] 32-bit words on the device")
     return allowed.data_ptr()

@@ -115,6 +115,18 @@ def test_binding_raises_value_error_on_invalid_argument():
         binding._check(binding.TS_ERR_HIP)
 
 
+def test_host_tensors_are_refused_without_a_library_call():
+    # the binding checks devices before it calls into the library: host tensors
+    # never reach a kernel (and there is no host path to fall back to)
+    import torch
+    import temperature_softmax_vocabulary_amd as tsv
+    x, t, u = torch.randn(2, 10), torch.ones(2), torch.rand(2, 3)
+    for call in (lambda: tsv.ts_softmax(x, t), lambda: tsv.ts_sample(x, u),
+                 lambda: tsv.ts_softmax_sample(x, t, u), lambda: tsv.ts_softmax_masked(x, t, None)):
+        with pytest.raises(ValueError, match="HIP device"):
+            call()
+
+
 def test_product_path_has_no_oracle_or_cpu_fallback():
     # The package never imports the oracle, and nothing under it names a CPU
     # softmax route: the binding only marshals arguments into the library.
