@@ -124,11 +124,10 @@ template <int F, int MODE>
 struct FusedOcc {
     // registers hold the current and the next chunk (8 F floats per lane)
     static constexpr int probs = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
-    // the draw sums need a few more: one wave per SIMD less keeps them in
-    // registers at 4096 and 8192 columns (the sums run at 4096 only for small
-    // calls, B V <= 2^21, whose grid is far below the device's capacity either
-    // way, and take 16384 where the plan says 8192)
-    static constexpr int waves_per_eu = MODE != kFusedProbsSums ? probs : (F == 4 ? 5 : (F == 8 ? 3 : probs));
+    // the draw sums need a few more: at 4096 columns one wave per SIMD less
+    // keeps them in registers (the sums run at 4096 only for small calls,
+    // B V <= 2^21, whose grid is far below the device's capacity either way)
+    static constexpr int waves_per_eu = MODE != kFusedProbsSums ? probs : (F == 4 ? 5 : probs);
 };
 
 template <int F, bool VEC, int MODE>

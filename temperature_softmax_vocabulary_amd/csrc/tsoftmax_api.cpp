@@ -338,20 +338,14 @@ ts_status launch_softmax(SoftmaxCall& call, const WsView& v, bool group_sums, bo
         int mode = tsk::kFusedProbs;
         int64_t grid = call.grid;
         if (group_sums && call.plan.F % 4 == 0) {   // chunks of whole draw groups
-            // With the draw sums, 16384-column chunks (two waves per SIMD, no
-            // spills) beat 8192 (four, spilling): 28.9 against 31.2 us for the
-            // whole call at B=64, V=262144.
-            int F = call.plan.F;
-            if (F == 8 && cdiv(a.V, 16384) <= tsk::kSlotStride) F = 16;
-            const int64_t nch = cdiv(a.V, 1024 * F);
+            // (at the plan's chunk: at 8192 columns the sums keep the plain
+            // mode's four waves per SIMD without spills, which beats 16384
+            // columns, two waves, at every batch measured)
             // this mode has its own occupancy: the grid must fit it too
             int64_t cap = 0;
-            ts_status st = resident_cap(tsk::kFusedProbsSums, F, call.vec, &cap);
+            ts_status st = resident_cap(tsk::kFusedProbsSums, call.plan.F, call.vec, &cap);
             if (st != TS_OK) return st;
-            if (nch <= cap) {   // else: the plain mode as planned, and a partials kernel later
-                call.plan.F = F;
-                a.nch = nch;
-                a.items = a.B * nch;
+            if (a.nch <= cap) {   // else: the plain mode as planned, and a partials kernel later
                 mode = tsk::kFusedProbsSums;
                 grid = fused_grid(a.items, a.nch, cap);
                 a.ngroups = cdiv(a.V, tsk::kDrawGroup);
