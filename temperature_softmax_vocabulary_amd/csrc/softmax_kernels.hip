@@ -81,9 +81,22 @@ __device__ __forceinline__ void combine_row(const float2* __restrict__ part, int
 }
 
 // ---------------------------------------------------------------------------
-// split, kernel 2: finalize fused into the write of the probs
+// split, rows of more than kSplitRowCombineMin chunks: one workgroup per row
+// combines its partials once into (shift, 1 / sum) for the write pass
 // ---------------------------------------------------------------------------
-template <int F, bool VEC>
+__global__ __launch_bounds__(NT) void ts_split_row_combine(SoftmaxArgs a) {
+    __shared__ float red[NW];
+    const int64_t row = blockIdx.x;
+    float gsh, r;
+    combine_row(a.part + row * a.nch, a.nch, exp2_scale(a.temps[row]), red, gsh, r);
+    if (threadIdx.x == 0) a.part[a.items + row] = make_float2(gsh, r);
+}
+
+// ---------------------------------------------------------------------------
+// split, kernel 2: finalize fused into the write of the probs (ROWSTAT: the
+// row's (shift, 1 / sum) from ts_split_row_combine; else combined here)
+// ---------------------------------------------------------------------------
+template <int F, bool VEC, bool ROWSTAT>
 __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
     __shared__ float red[NW];
     constexpr int C = NT * 4 * F;
@@ -96,7 +109,13 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
     load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x, kNegInf, mask_row(a, row));   // last use of logits
 
     float gsh, r;
-    combine_row(a.part + row * a.nch, a.nch, k, red, gsh, r);
+    if constexpr (ROWSTAT) {
+        const float2 st = a.part[a.items + row];
+        gsh = st.x;
+        r = st.y;
+    } else {
+        combine_row(a.part + row * a.nch, a.nch, k, red, gsh, r);
+    }
 #pragma unroll
     for (int i = 0; i < 4 * F; ++i) x[i] = exp2_hw((x[i] - gsh) * k) * r;
     store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
@@ -336,7 +355,14 @@ hipError_t split_impl(const SoftmaxArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((ts_split_partials<F, VEC>), grid, dim3(NT), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ts_split_finalize_write<F, VEC>), grid, dim3(NT), 0, s, a);
+    if (a.nch > kSplitRowCombineMin) {
+        hipLaunchKernelGGL(ts_split_row_combine, dim3(static_cast<uint32_t>(a.B)), dim3(NT), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((ts_split_finalize_write<F, VEC, true>), grid, dim3(NT), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((ts_split_finalize_write<F, VEC, false>), grid, dim3(NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 

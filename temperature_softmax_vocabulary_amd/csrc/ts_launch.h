@@ -11,6 +11,10 @@ namespace tsk {
 // (256 lanes x F float4 each).
 constexpr int kChunkThreads = 256;
 constexpr int kMinChunk = 1024;
+// Rows of more chunks than this get a row-combine kernel between the split's
+// two passes, so that each finalize workgroup reads its row's (shift, 1 / sum)
+// instead of combining all nch partials itself (nch^2 reads per row).
+constexpr int64_t kSplitRowCombineMin = 256;
 constexpr int kMaxChunk = 16384;
 
 // Slots per row for the in-kernel exchange (ts_exchange.h): the fused kernel
@@ -41,7 +45,8 @@ struct SoftmaxArgs {
     int64_t V;
     int64_t nch;           // chunks per row (split, fused)
     int64_t items;         // B * nch
-    float2* part;          // split: [B * nch] chunk partials (pm, pl)
+    float2* part;          // split: [B * nch] chunk partials (pm, pl), then for rows of
+                           // more than kSplitRowCombineMin chunks [B] (shift, 1 / sum)
     float4* gpart;         // fused with draw sums: [B * ngroups] per group, the sums of
                            // its probabilities held by each of the 4 waves
     float2* bpart;         // fused with draw sums: [B * ngroups * 64] (sum of probs, 0) per block

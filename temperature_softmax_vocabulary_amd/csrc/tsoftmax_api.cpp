@@ -319,7 +319,7 @@ ts_status prepare_softmax(const float* logits, const float* temps, const uint32_
         call->need_b = B;
     } else {
         if (a.items > INT32_MAX) return TS_ERR_INVALID_ARGUMENT;
-        call->need_p = a.items;
+        call->need_p = a.items + (a.nch > tsk::kSplitRowCombineMin ? B : 0);   // (+ per-row (shift, 1 / sum))
     }
     return TS_OK;
 }
@@ -512,7 +512,7 @@ TS_API ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream) {
     if (!sizes_ok(max_B, max_V)) return TS_ERR_INVALID_ARGUMENT;
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace* w = nullptr;
-    const int64_t split_parts = max_B * cdiv(max_V, tsk::kMinChunk);
+    const int64_t split_parts = max_B * cdiv(max_V, tsk::kMinChunk) + max_B;
     const int64_t parts = draw_parts(max_B, max_V);
     return ws_get(stream, max_B, split_parts > parts ? split_parts : parts, &w);
 }

@@ -279,3 +279,23 @@ def test_measurement_copy_is_exact(n, offset):
 def test_memory_params_for_the_recomputed_peak():
     clock_khz, bus_bits = tsv.ts_device_memory_params(DEV)
     assert clock_khz > 0 and bus_bits > 0
+
+
+@pytest.mark.parametrize("chunk", [1024, 2048])   # 293 chunks per row (row kernel), 147 (each workgroup)
+def test_split_rows_of_many_chunks(chunk):
+    # Rows of more than 256 chunks have their partials combined once per row
+    # by a kernel between the split's two passes; shorter rows combine them in
+    # every write workgroup. Rows masked from the start over 100 chunks, over
+    # one whole chunk, and everywhere but two ids (one in the last chunk).
+    rng = np.random.default_rng(61)
+    V = 293 * 1024 - 5
+    x = (rng.standard_normal((4, V)) * 4).astype(np.float32)
+    NEG = np.float32(-np.inf)
+    x[0, :100 * 1024] = NEG
+    x[1, 1024: 2 * 1024] = NEG
+    x[2, :] = NEG
+    x[2, [5000, V - 7]] = [0.5, 1.0]
+    t = np.array([0.5, 1.0, 1.3, 0.7], np.float32)
+    y = _run(x, t, tsv.TS_VARIANT_SPLIT, chunk).cpu().numpy()
+    assert_softmax_matches(y, x, t, what=f"split {chunk}")
+    _no_device_errors()
