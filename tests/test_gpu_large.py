@@ -16,7 +16,8 @@ paragraph for the definition, bug and fix paragraphs for masked chunks):
 Inputs are drawn on the device by torch's seeded generator (normal * 4,
 temperatures in [0.5, 1.5), seed B * 7 + V), with the masks of the pages'
 workloads: the first 16384 columns of row 0, a 20000-column block of the last
-row.
+row. The with-probabilities draw must write exactly ts_softmax's
+probabilities, and an all-ones allowed mask must change nothing.
 """
 import math
 
@@ -99,6 +100,14 @@ def test_largest_calls(B, V):
     u = torch.tensor([us], device=DEV).repeat(B, 1)
     _check_draws(x, t, tsv.ts_sample(y, u).cpu(), us, rows)
     _check_draws(x, t, tsv.ts_softmax_sample(x, t, u)[0].cpu(), us, rows)
+    # the draw that also writes the probabilities writes ts_softmax's, bit for bit
+    ids3, p3 = tsv.ts_softmax_sample(x, t, u, probs_out=True)
+    assert torch.equal(p3, y)
+    _check_draws(x, t, ids3.cpu(), us, rows)
+    del p3
+    # an all-ones allowed mask (2^26 words per row at the longest) changes nothing
+    ones = torch.full((B, (V + 31) // 32), -1, dtype=torch.int32, device=DEV)
+    assert torch.equal(tsv.ts_softmax_masked(x, t, ones), y)
     assert tsv.ts_device_errors() == 0
     del y
     torch.cuda.empty_cache()
