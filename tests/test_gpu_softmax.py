@@ -299,3 +299,40 @@ def test_split_rows_of_many_chunks(chunk):
     y = _run(x, t, tsv.TS_VARIANT_SPLIT, chunk).cpu().numpy()
     assert_softmax_matches(y, x, t, what=f"split {chunk}")
     _no_device_errors()
+
+
+SPLIT_IDS = [f"{tsv.VARIANT_NAMES[v]}-{c}" for v, c in SPLITS]
+
+
+@pytest.mark.parametrize("variant,chunk", SPLITS, ids=SPLIT_IDS)
+def test_closed_forms_on_the_gpu(variant, chunk):
+    # Closed forms of the definition (test paragraph) applied to the GPU
+    # itself, with no oracle in between:
+    #  - n equal finite logits (the rest -inf) give exactly 1/n: every
+    #    exponential is exp2(0) = 1 and a float sum of at most 2^24 ones is
+    #    exact, so each entry is 1/n within one rounding; masked entries are 0;
+    #  - two allowed ids give the logistic 1 / (1 + exp((b - a) / T)).
+    rng = np.random.default_rng(71)
+    V = 3 * 8192 + 389                      # several chunks and a ragged tail at every chunk size
+    NEG = np.float32(-np.inf)
+    x = np.full((7, V), NEG, np.float32)
+    x[0, :] = 2.5                                                   # the whole row
+    x[1, rng.choice(V, size=1000, replace=False)] = -3.0            # scattered ids
+    x[2, V - 300:] = 7.0                                            # the ragged tail only
+    x[3, :100] = 0.0                                                # the first chunk only
+    x[4, 12345] = 1.0                                               # a single id
+    a, b = 1.75, -0.5
+    x[5, [10, V - 10]] = [a, b]                                     # two ids, first and last chunk
+    x[6, [2047, 2048]] = [b, a]                                     # two ids across a chunk boundary
+    t = np.array([0.5, 1.0, 1.5, 0.7, 1.2, 0.8, 1.3], np.float32)
+    y = _run(x, t, variant, chunk).cpu().numpy()
+    fin = np.isfinite(x)
+    assert np.all(y[~fin] == 0)
+    for r in range(5):
+        want = np.float32(1.0) / np.float32(fin[r].sum())
+        got = y[r, fin[r]]
+        assert np.all(np.abs(got - want) <= np.spacing(want)), (r, got.min(), got.max(), want)
+    for r, (ia, ib) in ((5, (10, V - 10)), (6, (2048, 2047))):
+        pa = 1.0 / (1.0 + np.exp((np.float64(b) - np.float64(a)) / np.float64(t[r])))
+        np.testing.assert_allclose(y[r, ia], pa, rtol=1e-5)
+        np.testing.assert_allclose(y[r, ib], 1.0 - pa, rtol=1e-5)
