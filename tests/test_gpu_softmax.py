@@ -301,9 +301,6 @@ def test_split_rows_of_many_chunks(chunk):
     _no_device_errors()
 
 
-SPLIT_IDS = [f"{tsv.VARIANT_NAMES[v]}-{c}" for v, c in SPLITS]
-
-
 @pytest.mark.parametrize("variant,chunk", SPLITS, ids=SPLIT_IDS)
 def test_closed_forms_on_the_gpu(variant, chunk):
     # Closed forms of the definition (test paragraph) applied to the GPU
