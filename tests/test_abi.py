@@ -140,8 +140,9 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
 @pytest.mark.parametrize("B,V,expect", [
     (1, 16384, (binding.TS_VARIANT_ROWWISE, 0)),            # the row fits one workgroup's registers
     (64, 5003, (binding.TS_VARIANT_ROWWISE, 0)),
-    (1, 151936, (binding.TS_VARIANT_FUSED, 4096)),           # B*V <= 2^21: latency-bound, small chunks
-    (8, 262144, (binding.TS_VARIANT_FUSED, 4096)),           # exactly 2^21
+    (1, 151936, (binding.TS_VARIANT_FUSED, 4096)),           # B*V <= 2^20: latency-bound, small chunks
+    (4, 262144, (binding.TS_VARIANT_FUSED, 4096)),           # exactly 2^20
+    (8, 201088, (binding.TS_VARIANT_FUSED, 8192)),           # 1.6e6 elements
     (16, 201088, (binding.TS_VARIANT_FUSED, 8192)),
     (64, 262144, (binding.TS_VARIANT_FUSED, 8192)),          # the bench workload
     (2, 2 * 1024 * 1024 + 4099, (binding.TS_VARIANT_FUSED, 16384)),   # > 256 chunks of 8192
