@@ -145,7 +145,7 @@ struct FusedOcc {
     static constexpr int probs = F <= 2 ? 8 : (F == 4 ? 6 : (F == 8 ? 4 : 2));
     // the draw sums need a few more: at 4096 columns one wave per SIMD less
     // keeps them in registers (the sums run at 4096 only for small calls,
-    // B V <= 2^20, whose grid is far below the device's capacity either way)
+    // B V <= 2^21, whose grid is far below the device's capacity either way)
     static constexpr int waves_per_eu = MODE != kFusedProbsSums ? probs : (F == 4 ? 5 : probs);
 };
 

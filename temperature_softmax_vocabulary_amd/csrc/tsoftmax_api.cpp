@@ -209,9 +209,10 @@ ts_status fused_fits(int F, bool vec, int64_t V, bool on_device, bool* fits) {
 // 201088, 262144} (and, by graph replay, B in 2..16 around the first edge):
 //  - a row that fits one workgroup's registers: one workgroup per row (single
 //    read, no partials);
-//  - B*V <= 2^20 elements: fused, 4096-column chunks (the call is bound by
-//    latency; more, smaller workgroups; beyond about 1.1e6 elements 8192
-//    columns are as fast or faster);
+//  - B*V <= 2^20 elements, or 2^21 for rows of at most 65536 columns: fused,
+//    4096-column chunks (the call is bound by latency; more, smaller
+//    workgroups; beyond that 8192 columns are as fast or faster, by graph
+//    replay at B in 2..256);
 //  - larger: fused, 8192-column chunks (four workgroups per CU hide the waits
 //    better than two of 16384 columns, and a short last chunk wastes less:
 //    at B=64 it is 22.7 against 23.2 us for V=262144 and 14.7 against 17.6 us
@@ -224,7 +225,8 @@ ts_status choose_plan(int64_t B, int64_t V, bool vec, bool on_device, Plan* p) {
         *p = Plan{TS_VARIANT_ROWWISE, 0};
         return TS_OK;
     }
-    for (int F = B * V <= (int64_t(1) << 20) ? 4 : 8; F <= 16; F *= 2) {
+    const int64_t small = V <= 65536 ? (int64_t(1) << 21) : (int64_t(1) << 20);
+    for (int F = B * V <= small ? 4 : 8; F <= 16; F *= 2) {
         bool fits = false;
         const ts_status st = fused_fits(F, vec, V, on_device, &fits);
         if (st != TS_OK) return st;

@@ -143,6 +143,8 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
     (1, 151936, (binding.TS_VARIANT_FUSED, 4096)),           # B*V <= 2^20: latency-bound, small chunks
     (4, 262144, (binding.TS_VARIANT_FUSED, 4096)),           # exactly 2^20
     (8, 201088, (binding.TS_VARIANT_FUSED, 8192)),           # 1.6e6 elements
+    (64, 32768, (binding.TS_VARIANT_FUSED, 4096)),           # short rows: 4096 up to 2^21
+    (65, 32768, (binding.TS_VARIANT_FUSED, 8192)),
     (16, 201088, (binding.TS_VARIANT_FUSED, 8192)),
     (64, 262144, (binding.TS_VARIANT_FUSED, 8192)),          # the bench workload
     (2, 2 * 1024 * 1024 + 4099, (binding.TS_VARIANT_FUSED, 16384)),   # > 256 chunks of 8192
