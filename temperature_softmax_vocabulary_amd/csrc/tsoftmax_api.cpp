@@ -208,7 +208,8 @@ ts_status fused_fits(int F, bool vec, int64_t V, bool on_device, bool* fits) {
 // chunk size over B in {1, 3, 8, 16, 32, 64, 128, 256} and V in {151936,
 // 201088, 262144} (and, by graph replay, B in 2..16 around the first edge):
 //  - a row that fits one workgroup's registers: one workgroup per row (single
-//    read, no partials);
+//    read, no partials), but the fused split for 768..2048 such rows of at
+//    least 4096 columns;
 //  - B*V <= 2^20 elements, or 2^21 for rows of at most 65536 columns: fused,
 //    4096-column chunks (the call is bound by latency; more, smaller
 //    workgroups; beyond that 8192 columns are as fast or faster, by graph
@@ -222,6 +223,19 @@ ts_status fused_fits(int F, bool vec, int64_t V, bool on_device, bool* fits) {
 //    else the split pair, which never waits.
 ts_status choose_plan(int64_t B, int64_t V, bool vec, bool on_device, Plan* p) {
     if (V <= tsk::kRowwiseResidentMaxV) {
+        // except for 768..2048 rows of 4096..16384 columns: there the row
+        // kernel's 1024-lane workgroups fill the device in uneven rounds, and
+        // the fused split was 1-12 % faster (by graph replay)
+        if (V >= 4096 && B >= 768 && B <= 2048) {
+            const int F = V > 4096 ? 8 : 4;
+            bool fits = false;
+            const ts_status st = fused_fits(F, vec, V, on_device, &fits);
+            if (st != TS_OK) return st;
+            if (fits) {
+                *p = Plan{TS_VARIANT_FUSED, F};
+                return TS_OK;
+            }
+        }
         *p = Plan{TS_VARIANT_ROWWISE, 0};
         return TS_OK;
     }

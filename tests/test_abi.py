@@ -140,6 +140,11 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
 @pytest.mark.parametrize("B,V,expect", [
     (1, 16384, (binding.TS_VARIANT_ROWWISE, 0)),            # the row fits one workgroup's registers
     (64, 5003, (binding.TS_VARIANT_ROWWISE, 0)),
+    (767, 16384, (binding.TS_VARIANT_ROWWISE, 0)),           # short rows: one workgroup per row ...
+    (768, 16384, (binding.TS_VARIANT_FUSED, 8192)),          # ... except 768..2048 rows of 4096..16384
+    (2048, 4096, (binding.TS_VARIANT_FUSED, 4096)),
+    (2049, 4096, (binding.TS_VARIANT_ROWWISE, 0)),
+    (1024, 4095, (binding.TS_VARIANT_ROWWISE, 0)),
     (1, 151936, (binding.TS_VARIANT_FUSED, 4096)),           # B*V <= 2^20: latency-bound, small chunks
     (4, 262144, (binding.TS_VARIANT_FUSED, 4096)),           # exactly 2^20
     (8, 201088, (binding.TS_VARIANT_FUSED, 8192)),           # 1.6e6 elements

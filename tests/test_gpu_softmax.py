@@ -190,12 +190,14 @@ def test_long_rows_default_plan(V):
     assert plan[0] == expect
 
 
-@pytest.mark.parametrize("B,V", [(4, 16384), (4, 16385), (4, 262144), (4, 262148), (64, 32768), (65, 32768),
+@pytest.mark.parametrize("B,V", [(4, 16384), (4, 16385), (767, 16384), (768, 16384), (2048, 4096), (2049, 4096),
+                                 (4, 262144), (4, 262148), (64, 32768), (65, 32768),
                                  (2, 256 * 8192), (2, 256 * 8192 + 4)])
 def test_default_plan_at_thresholds(B, V):
     # each side of every edge of the work-split table: rowwise up to 16384
-    # columns, fused 4096 up to 2^20 elements (2^21 for rows of at most 65536
-    # columns), fused 8192 up to 256 chunks a row
+    # columns (but fused for 768..2048 rows of 4096..16384 columns), fused
+    # 4096 up to 2^20 elements (2^21 for rows of at most 65536 columns), fused
+    # 8192 up to 256 chunks a row
     w = workloads.make(B, V, "quarters" if B >= 4 else "first16384")
     plan = tsv.ts_plan(B, V)
     print(f"[gpu] threshold B={B} V={V} plan={plan}", flush=True)
