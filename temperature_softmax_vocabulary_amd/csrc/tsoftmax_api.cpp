@@ -206,7 +206,8 @@ ts_status fused_fits(int F, bool vec, int64_t V, bool on_device, bool* fits) {
 
 // The work-split table, from cold timings on MI355X of every variant and
 // chunk size over B in {1, 3, 8, 16, 32, 64, 128, 256} and V in {151936,
-// 201088, 262144} (and, by graph replay, B in 2..16 around the first edge):
+// 201088, 262144}, and by graph replay around each edge (B in 2..16 for those
+// V; B in 16..256 for V of 32000..65536; B in 16..4096 for V of 4096..16384):
 //  - a row that fits one workgroup's registers: one workgroup per row (single
 //    read, no partials), but the fused split for 768..2048 such rows of at
 //    least 4096 columns;
