@@ -201,6 +201,14 @@ def _elapsed_us(torch, fn, n):
     return e0.elapsed_time(e1) * 1000.0 / n
 
 
+def _side_us(torch, fn, n=500, reps=3, warmup=30):
+    """µs per call of a side measurement: warm-up calls, then the median of
+    `reps` timed runs of n calls (steadier than one short run)."""
+    for i in range(warmup):
+        fn(i)
+    return statistics.median(_elapsed_us(torch, fn, n) for _ in range(reps))
+
+
 def graph_cold_us(torch, tsv, dev, w, op: str = "softmax") -> float:
     """µs per call of ts_softmax (op="softmax") or of the same-bytes copy
     (op="copy") on workload w, cold, from graph replay (launch gaps removed):
@@ -604,9 +612,7 @@ def main(argv=None) -> int:
         # hot: the same buffers every call (how the page timed, graph replays of one input)
         def hot(i):
             step(0)
-        for i in range(20):
-            hot(i)
-        extras["hot_us_per_call"] = round(_elapsed_us(torch, hot, 200), 3)
+        extras["hot_us_per_call"] = round(_side_us(torch, hot), 3)
         # graph replay of the same rotating calls (launch gaps removed)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -633,17 +639,13 @@ def main(argv=None) -> int:
         # with and without writing the probabilities (cold, rotating sets)
         u = torch.from_numpy(w.uniforms).to(dev)
         ids = torch.empty((B, w.uniforms.shape[1]), dtype=torch.int32, device=dev)
-        for i in range(10):
-            tsv.ts_sample(ys[i % nsets], u, out_ids=ids)
         extras["sample_us_per_call"] = round(
-            _elapsed_us(torch, lambda i: tsv.ts_sample(ys[i % nsets], u, out_ids=ids), 200), 3)
-        for i in range(10):
-            tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids)
+            _side_us(torch, lambda i: tsv.ts_sample(ys[i % nsets], u, out_ids=ids)), 3)
         extras["softmax_sample_ids_only_us_per_call"] = round(
-            _elapsed_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids), 200), 3)
+            _side_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids)), 3)
         extras["softmax_sample_with_probs_us_per_call"] = round(
-            _elapsed_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids,
-                                                               probs_out=ys[i % nsets]), 200), 3)
+            _side_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids,
+                                                            probs_out=ys[i % nsets])), 3)
         # the same masks applied from an allowed-id bitmask while the logits are read
         # (finite logits everywhere, B * ceil(V/32) * 4 extra bytes read)
         # (cold like the timed region: the logit and mask buffers rotate too)
@@ -655,9 +657,7 @@ def main(argv=None) -> int:
         def masked(i):
             j = i % nsets
             tsv.ts_softmax_masked(xms[j], ts[j], bitss[j], out=ys[j])
-        for i in range(10):
-            masked(i)
-        extras["masked_bitmask_us_per_call"] = round(_elapsed_us(torch, masked, 200), 3)
+        extras["masked_bitmask_us_per_call"] = round(_side_us(torch, masked), 3)
         del xms, bitss
         # every workload, graph replay (the small ones are launch-bound)
         extras["configs_graph_us_per_call"] = configs_graph_us(torch, tsv, workloads, dev)
