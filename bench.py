@@ -609,6 +609,15 @@ def main(argv=None) -> int:
         extras["copy_GBps"] = round(bytes_per_call / cus / 1e3, 1)
         extras["softmax_over_copy"] = round(cus / us, 4)
     if args.extras == "all":
+        # the softmax and the same-bytes copy in 7 interleaved runs of 200 cold
+        # calls each: medians, and the median of the per-run ratios
+        runs = []
+        for _ in range(7):
+            runs.append((_elapsed_us(torch, step, 200), _elapsed_us(torch, cp, 200)))
+        extras["interleaved_7x200"] = {
+            "softmax_us_median": round(statistics.median(r[0] for r in runs), 3),
+            "copy_us_median": round(statistics.median(r[1] for r in runs), 3),
+            "softmax_over_copy_median": round(statistics.median(r[1] / r[0] for r in runs), 4)}
         # hot: the same buffers every call (how the page timed, graph replays of one input)
         def hot(i):
             step(0)
