@@ -210,22 +210,35 @@ def _side_us(torch, fn, n=500, reps=3, warmup=30):
 
 
 def graph_cold_us(torch, tsv, dev, w, op: str = "softmax") -> float:
-    """µs per call of ts_softmax (op="softmax") or of the same-bytes copy
-    (op="copy") on workload w, cold, from graph replay (launch gaps removed):
-    rotating slices of one >= 512 MiB buffer pair, all captured into one
-    graph."""
+    """µs per call, cold, from graph replay (launch gaps removed): rotating
+    slices of one >= 512 MiB buffer pair, all captured into one graph. op:
+    "softmax" (ts_softmax), "copy" (the same-bytes copy), "sample" (ts_sample
+    on the slices' probabilities), "ids" and "probs" (ts_softmax_sample
+    without and with writing the probabilities), with w's uniforms."""
     B, V = w.B, w.V
     nsets = min(512, max(2, math.ceil((512 << 20) / (2 * B * V * 4))))
     x = torch.from_numpy(w.logits).to(dev).unsqueeze(0).repeat(nsets, 1, 1)
     t = torch.from_numpy(w.temps).to(dev)
     y = torch.empty_like(x)
+    u = torch.from_numpy(w.uniforms).to(dev)
+    ids = torch.empty((nsets, B, u.shape[1]), dtype=torch.int32, device=dev)
     s = torch.cuda.Stream(device=dev)
     tsv.ts_reserve(B, V, device=dev, stream=s)
+    if op == "sample":
+        with torch.cuda.stream(s):
+            for i in range(nsets):
+                tsv.ts_softmax(x[i], t, out=y[i])
 
     def calls():
         for i in range(nsets):
             if op == "copy":
                 tsv.ts_copy_f32(x[i], y[i])
+            elif op == "sample":
+                tsv.ts_sample(y[i], u, out_ids=ids[i])
+            elif op == "ids":
+                tsv.ts_softmax_sample(x[i], t, u, out_ids=ids[i])
+            elif op == "probs":
+                tsv.ts_softmax_sample(x[i], t, u, out_ids=ids[i], probs_out=y[i])
             else:
                 tsv.ts_softmax(x[i], t, out=y[i])
     with torch.cuda.stream(s):
@@ -244,7 +257,7 @@ def graph_cold_us(torch, tsv, dev, w, op: str = "softmax") -> float:
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1000.0 / (reps * nsets)
-    del x, y, g
+    del x, y, ids, g
     return round(us, 3)
 
 
@@ -670,6 +683,11 @@ def main(argv=None) -> int:
         del xms, bitss
         # every workload, graph replay (the small ones are launch-bound)
         extras["configs_graph_us_per_call"] = configs_graph_us(torch, tsv, workloads, dev)
+        # the draws on every workload (64 uniforms per row), graph replay
+        extras["configs_graph_draw_us_per_call"] = {
+            name: {op: graph_cold_us(torch, tsv, dev, workloads.make_config(name), op)
+                   for op in ("sample", "ids", "probs")}
+            for name in workloads.CONFIG_ORDER}
         dp = torch.cuda.get_device_properties(dev)
         clock_khz, bus_bits = tsv.ts_device_memory_params(dev)
         extras["device"] = {"name": dp.name, "cus": dp.multi_processor_count,
