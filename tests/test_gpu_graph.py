@@ -116,3 +116,30 @@ def test_graph_survives_later_workspace_growth():
         assert_softmax_matches(got, w.logits, w.temps, what=f"replay {rep}")
         assert_ids_valid(ids.cpu().numpy(), got, w.uniforms, what=f"replay {rep}")
     assert tsv.ts_device_errors(device=DEV, stream=s) == 0
+
+
+def test_capture_split_with_row_combine():
+    # rows of more than 256 chunks: the split runs three kernels (partials,
+    # one row-combine workgroup per row, write); all three are captured
+    B, V, chunk = 3, 293 * 1024 - 5, 1024
+    s = torch.cuda.Stream(device=DEV)
+    tsv.ts_reserve(B, V, device=DEV, stream=s)
+    x = torch.zeros((B, V), dtype=torch.float32, device=DEV)
+    t = torch.ones((B,), dtype=torch.float32, device=DEV)
+    y = torch.empty_like(x)
+    with torch.cuda.stream(s):
+        tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_SPLIT, chunk, out=y)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_SPLIT, chunk, out=y)
+    for rep in range(3):
+        w = workloads.make(B, V, "first16384", seed=700 + rep)
+        x.copy_(torch.from_numpy(w.logits))
+        t.copy_(torch.from_numpy(w.temps))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, what=f"replay {rep}")
+        _ = (x * 2).sum().item()   # eager work between replays
+    assert tsv.ts_device_errors(device=DEV, stream=s) == 0
