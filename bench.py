@@ -512,7 +512,7 @@ def main(argv=None) -> int:
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the softmax is sharded across GPUs by row or by vocabulary slice; "
-              "this build measures one GPU's share)", file=sys.stderr)
+              "the benchmark measures one GPU's share)", file=sys.stderr)
         return 2
 
     import torch

@@ -1,7 +1,8 @@
 """Float64 CPU oracle for the temperature softmax over a vocabulary and for the
 inverse-CDF draw that consumes it.
 
-TEST INFRASTRUCTURE. This module is the checker, not the product. Only code
+TEST INFRASTRUCTURE. This module is what the tests compare against, not the
+product. Only code
 under ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import or call it. The HIP library never calls it, never links
 it, and shares no code, table or helper with it; the product path has no CPU
