@@ -2,11 +2,10 @@
 inverse-CDF draw that consumes it.
 
 TEST INFRASTRUCTURE. This module is what the tests compare against, not the
-product. Only code
-under ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
-``bench.py`` may import or call it. The HIP library never calls it, never links
-it, and shares no code, table or helper with it; the product path has no CPU
-fallback.
+product. Only code under ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call it. The HIP library
+never calls it, never links it, and shares no code, table or helper with it;
+the product path has no CPU fallback.
 
 It is deliberately plain and slow: numpy float64, one library primitive per
 step, no blocking, no chunking, no fusion.
