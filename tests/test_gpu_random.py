@@ -101,3 +101,55 @@ def test_random_case(seed):
         assert_ids_valid(ids.cpu().numpy(), p32, u, what=f"{what} {w}")
         assert np.all(np.isfinite(x)[np.arange(B)[:, None], ids.cpu().numpy()]), f"{what} {w}"
     assert tsv.ts_device_errors() == 0
+
+
+def _many_rows_case(seed):
+    """Many short rows and many draws: B up to 2048 (around the 768..2048 rows
+    that take the fused split for 4096..16384 columns), V up to 20000,
+    K up to 1100 (the resolve that shares level 1 across a row's targets)."""
+    rng = np.random.default_rng(10_000 + seed)
+    V = int(rng.choice([4096, 4097, 8191, 8192, 12000, 16384, 16383])) if rng.random() < 0.5 \
+        else int(rng.integers(1, 20001))
+    B = int(rng.choice([767, 768, 1024, 2048, 2049])) if rng.random() < 0.4 else int(rng.integers(1, 2049))
+    B = max(1, min(B, 4_000_000 // V))
+    x = (rng.standard_normal((B, V)) * rng.choice([1.0, 4.0])).astype(np.float32)
+    NEG = np.float32(-np.inf)
+    kinds = rng.integers(0, 5, size=B)
+    for r in np.nonzero(kinds == 1)[0]:                      # masked from the start
+        x[r, : int(rng.integers(1, V + 1))] = NEG
+    for r in np.nonzero(kinds == 2)[0]:                      # three allowed ids
+        keep = rng.choice(V, size=min(V, 3), replace=False)
+        vals = x[r, keep].copy()
+        x[r, :] = NEG
+        x[r, keep] = vals
+    for r in np.nonzero(kinds == 3)[0]:                      # the row's last columns
+        x[r, V - int(rng.integers(1, min(V, 5) + 1)):] = NEG
+    x[~np.isfinite(x).any(axis=1), 0] = 1.0
+    t = (10.0 ** rng.uniform(-1.0, 0.7, size=B)).astype(np.float32)
+    K = int(rng.choice([1, 16, 64, 300, 1100]))
+    return x, t, rng.random((B, K), dtype=np.float32)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_many_rows_case(seed):
+    x, t, u = _many_rows_case(seed)
+    B, V = x.shape
+    what = f"many-rows case {seed} B={B} V={V} K={u.shape[1]} plan={tsv.ts_plan(B, V)}"
+    print(f"[gpu] {what}", flush=True)
+    ref = softmax_ref(x, t)
+    xd, td, ud = (torch.from_numpy(a).to(DEV) for a in (x, t, u))
+    y = tsv.ts_softmax(xd, td)
+    bits = workloads.pack_allowed(np.isfinite(x)).view(np.int32)
+    xm = np.where(np.isfinite(x), x, np.float32(0.0)).astype(np.float32)
+    ym = tsv.ts_softmax_masked(torch.from_numpy(xm).to(DEV), td, torch.from_numpy(bits).to(DEV))
+    ids = tsv.ts_sample(y, ud)
+    ids2, yp = tsv.ts_softmax_sample(xd, td, ud, probs_out=True)
+    ids3, _ = tsv.ts_softmax_sample(xd, td, ud)
+    torch.cuda.synchronize()
+    assert_softmax_matches(y.cpu().numpy(), x, t, ref, what=what)
+    assert torch.equal(ym, y), what
+    assert_softmax_matches(yp.cpu().numpy(), x, t, ref, what=f"{what} with draw")
+    p32 = ref.astype(np.float32)
+    for i, name in ((ids, "sample"), (ids2, "with probs"), (ids3, "ids only")):
+        assert_ids_valid(i.cpu().numpy(), p32, u, what=f"{what} {name}")
+    assert tsv.ts_device_errors() == 0
