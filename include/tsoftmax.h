@@ -182,9 +182,14 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  * logits, temps : as for ts_softmax.
  * allowed       : NULL, or an allowed-id bitmask as for ts_softmax_masked.
  * uniforms      : [B, K] float32, as for ts_sample.
- * probs_out     : [B, V] float32 or NULL. If not NULL it receives the same
- *                 probabilities ts_softmax computes (probs_out == logits is
- *                 allowed); if NULL the probabilities are never written.
+ * probs_out     : [B, V] float32 or NULL. If not NULL it receives the
+ *                 probabilities of ts_softmax (probs_out == logits is
+ *                 allowed): the same bits where ts_plan gives the fused or
+ *                 split kernels; rows it gives the one-workgroup-per-row
+ *                 kernel are computed here by the fused split instead (which
+ *                 leaves the draw its group sums), whose bits agree with
+ *                 ts_softmax's to the same tolerance. If NULL the
+ *                 probabilities are never written.
  * out_ids       : [B, K] int32. The inverse-CDF rule of ts_sample with the
  *                 same three levels of integer prefix sums; every id
  *                 drawn has a finite logit (and an allowed bit); -1 for a row

@@ -432,9 +432,12 @@ hipError_t launch_rowwise(const SoftmaxArgs& a, bool vec, hipStream_t s) {
     } else if (a.V <= RT * 4 * 2) {
         if (vec) hipLaunchKernelGGL((ts_rowwise_resident<RT, 2, true>), grid, dim3(RT), 0, s, a);
         else hipLaunchKernelGGL((ts_rowwise_resident<RT, 2, false>), grid, dim3(RT), 0, s, a);
-    } else if (a.V <= kRowwiseResidentMaxV) {
+    } else if (a.V <= RT * 4 * 4) {
         if (vec) hipLaunchKernelGGL((ts_rowwise_resident<RT, 4, true>), grid, dim3(RT), 0, s, a);
         else hipLaunchKernelGGL((ts_rowwise_resident<RT, 4, false>), grid, dim3(RT), 0, s, a);
+    } else if (a.V <= kRowwiseRegisterMaxV) {
+        if (vec) hipLaunchKernelGGL((ts_rowwise_resident<RT, 8, true>), grid, dim3(RT), 0, s, a);
+        else hipLaunchKernelGGL((ts_rowwise_resident<RT, 8, false>), grid, dim3(RT), 0, s, a);
     } else {
         if (vec) hipLaunchKernelGGL((ts_rowwise_stream<RT, true>), grid, dim3(RT), 0, s, a);
         else hipLaunchKernelGGL((ts_rowwise_stream<RT, false>), grid, dim3(RT), 0, s, a);

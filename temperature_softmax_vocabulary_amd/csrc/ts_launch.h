@@ -31,8 +31,11 @@ constexpr int kDrawBlock = 64;
 constexpr int kDrawGroup = 4096;
 constexpr int kBlocksPerGroup = kDrawGroup / kDrawBlock;
 
-// Largest row the resident one-workgroup-per-row kernel holds in registers.
+// One workgroup per row: rows of up to kRowwiseRegisterMaxV columns sit in
+// its registers (read once); longer rows are streamed twice. The work-split
+// table picks this kernel by default for rows of up to kRowwiseResidentMaxV.
 constexpr int kRowwiseThreads = 1024;
+constexpr int64_t kRowwiseRegisterMaxV = 32768;
 constexpr int64_t kRowwiseResidentMaxV = 16384;
 
 struct SoftmaxArgs {

@@ -207,10 +207,11 @@ ts_status fused_fits(int F, bool vec, int64_t V, bool on_device, bool* fits) {
 // The work-split table, from cold timings on MI355X of every variant and
 // chunk size over B in {1, 3, 8, 16, 32, 64, 128, 256} and V in {151936,
 // 201088, 262144}, and by graph replay around each edge (B in 2..16 for those
-// V; B in 16..256 for V of 32000..65536; B in 16..4096 for V of 4096..16384):
+// V; B in 16..256 for V of 32000..65536; B in 16..4096 for V of 4096..32768):
 //  - a row that fits one workgroup's registers: one workgroup per row (single
 //    read, no partials), but the fused split for 768..2048 such rows of at
-//    least 4096 columns;
+//    least 4096 columns; for rows of 16385..32768 columns only where it was
+//    measured faster;
 //  - B*V <= 2^20 elements, or 2^21 for rows of at most 65536 columns: fused,
 //    4096-column chunks (the call is bound by latency; more, smaller
 //    workgroups; beyond that 8192 columns are as fast or faster, by graph
@@ -240,6 +241,15 @@ ts_status choose_plan(int64_t B, int64_t V, bool vec, bool on_device, Plan* p) {
         *p = Plan{TS_VARIANT_ROWWISE, 0};
         return TS_OK;
     }
+    // rows of 16385..32768 columns still fit the row kernel's registers (8
+    // values a lane); it was 2-21 % faster than the fused split for at least
+    // 128 rows of up to 20480 columns and for at least 2048 rows of any such
+    // length, and up to 13 % slower elsewhere (rows of 3 or 4 whole
+    // 8192-column chunks at 512..1536 rows), by graph replay
+    if (V <= tsk::kRowwiseRegisterMaxV && (B >= 2048 || (V <= 20480 && B >= 128))) {
+        *p = Plan{TS_VARIANT_ROWWISE, 0};
+        return TS_OK;
+    }
     const int64_t small = V <= 65536 ? (int64_t(1) << 21) : (int64_t(1) << 20);
     for (int F = B * V <= small ? 4 : 8; F <= 16; F *= 2) {
         bool fits = false;
@@ -252,6 +262,21 @@ ts_status choose_plan(int64_t B, int64_t V, bool vec, bool on_device, Plan* p) {
     }
     *p = Plan{TS_VARIANT_SPLIT, 16};
     return TS_OK;
+}
+
+// The softmax ahead of a draw that also writes the probabilities: the fused
+// split leaves the draw's group sums of the probabilities, which the draw
+// otherwise reads the probabilities once more to form, so rows the table
+// gives the row kernel take the fused split here when it fits.
+ts_status choose_draw_plan(int64_t B, int64_t V, bool vec, Plan* p) {
+    ts_status st = choose_plan(B, V, vec, true, p);
+    if (st != TS_OK || p->variant != TS_VARIANT_ROWWISE) return st;
+    const int64_t small = V <= 65536 ? (int64_t(1) << 21) : (int64_t(1) << 20);
+    const int F = B * V <= small || V <= 4096 ? 4 : 8;
+    bool fits = false;
+    st = fused_fits(F, vec, V, true, &fits);
+    if (st == TS_OK && fits) *p = Plan{TS_VARIANT_FUSED, F};
+    return st;
 }
 
 // Fused grid: one workgroup per item while the device holds them all at once;
@@ -278,7 +303,7 @@ struct SoftmaxCall {
 
 // Argument checks and the work split; launches nothing. B > 0.
 ts_status prepare_softmax(const float* logits, const float* temps, const uint32_t* allowed, int64_t B, int64_t V,
-                          float* out, int variant, int chunk, SoftmaxCall* call) {
+                          float* out, int variant, int chunk, SoftmaxCall* call, bool for_draw = false) {
     if (!logits || !temps || !out) return TS_ERR_INVALID_ARGUMENT;
     const int64_t xbytes = B * V * 4;
     if (out != logits && overlaps(out, xbytes, logits, xbytes)) return TS_ERR_INVALID_ARGUMENT;
@@ -295,7 +320,7 @@ ts_status prepare_softmax(const float* logits, const float* temps, const uint32_
 
     Plan plan{variant, F};
     if (variant == TS_VARIANT_AUTO) {
-        ts_status st = choose_plan(B, V, vec, true, &plan);
+        ts_status st = for_draw ? choose_draw_plan(B, V, vec, &plan) : choose_plan(B, V, vec, true, &plan);
         if (st != TS_OK) return st;
         if (F != 0 && plan.variant != TS_VARIANT_ROWWISE) plan.F = F;
     }
@@ -513,7 +538,7 @@ TS_API ts_status ts_softmax_sample(const float* logits, const float* temps, cons
     // probabilities and ids: the softmax (the fused split also leaves the group
     // sums of the probabilities), then the draw on the written probabilities
     SoftmaxCall call;
-    ts_status st = prepare_softmax(logits, temps, allowed, B, V, probs_out, TS_VARIANT_AUTO, 0, &call);
+    ts_status st = prepare_softmax(logits, temps, allowed, B, V, probs_out, TS_VARIANT_AUTO, 0, &call, true);
     if (st != TS_OK) return st;
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace* w = nullptr;

@@ -145,6 +145,12 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
     (2048, 4096, (binding.TS_VARIANT_FUSED, 4096)),
     (2049, 4096, (binding.TS_VARIANT_ROWWISE, 0)),
     (1024, 4095, (binding.TS_VARIANT_ROWWISE, 0)),
+    (127, 20480, (binding.TS_VARIANT_FUSED, 8192)),          # 16385..32768 columns: fused, but one
+    (128, 20480, (binding.TS_VARIANT_ROWWISE, 0)),           # workgroup per row from 128 rows up
+    (128, 20484, (binding.TS_VARIANT_FUSED, 8192)),          # to 20480 columns ...
+    (2047, 32768, (binding.TS_VARIANT_FUSED, 8192)),
+    (2048, 32768, (binding.TS_VARIANT_ROWWISE, 0)),          # ... and from 2048 rows up to 32768
+    (2048, 32772, (binding.TS_VARIANT_FUSED, 8192)),
     (1, 151936, (binding.TS_VARIANT_FUSED, 4096)),           # B*V <= 2^20: latency-bound, small chunks
     (4, 262144, (binding.TS_VARIANT_FUSED, 4096)),           # exactly 2^20
     (8, 201088, (binding.TS_VARIANT_FUSED, 8192)),           # 1.6e6 elements

@@ -191,11 +191,13 @@ def test_long_rows_default_plan(V):
 
 
 @pytest.mark.parametrize("B,V", [(4, 16384), (4, 16385), (767, 16384), (768, 16384), (2048, 4096), (2049, 4096),
-                                 (4, 262144), (4, 262148), (64, 32768), (65, 32768),
+                                 (127, 20480), (128, 20480), (128, 20484), (2047, 32768), (2048, 32768),
+                                 (2048, 32772), (4, 262144), (4, 262148), (64, 32768), (65, 32768),
                                  (2, 256 * 8192), (2, 256 * 8192 + 4)])
 def test_default_plan_at_thresholds(B, V):
     # each side of every edge of the work-split table: rowwise up to 16384
-    # columns (but fused for 768..2048 rows of 4096..16384 columns), fused
+    # columns (but fused for 768..2048 rows of 4096..16384 columns), and up
+    # to 32768 columns from 128 rows (20480 columns) or 2048 rows, fused
     # 4096 up to 2^20 elements (2^21 for rows of at most 65536 columns), fused
     # 8192 up to 256 chunks a row
     w = workloads.make(B, V, "quarters" if B >= 4 else "first16384")
@@ -246,6 +248,23 @@ def test_rowwise_many_short_rows():
     torch.cuda.synchronize()
     rows = np.arange(0, w.B, 97)
     _sampled_rows_match(y, w, rows)
+
+
+@pytest.mark.parametrize("B,V", [(3, 16385), (5, 20000), (2, 32000), (3, 32767), (4, 32768), (2, 32772)])
+def test_rowwise_forced_register_edges(B, V):
+    # the forced one-workgroup-per-row kernel on each side of its register
+    # limits (8 values a lane up to 32768 columns, streamed above), aligned
+    # and not, plain and with an allowed-id mask
+    w = workloads.make(B, V, "quarters" if B >= 4 else "first16384")
+    print(f"[gpu] rowwise forced B={B} V={V}", flush=True)
+    y = _run(w.logits, w.temps, tsv.TS_VARIANT_ROWWISE, 0).cpu().numpy()
+    assert_softmax_matches(y, w.logits, w.temps, what=f"rowwise B={B} V={V}")
+    xm = torch.from_numpy(workloads.unmasked_logits(w)).to(DEV)
+    bits = torch.from_numpy(workloads.make_allowed(w).view(np.int32).copy()).to(DEV)
+    ym = tsv.ts_softmax_variant(xm, torch.from_numpy(w.temps).to(DEV), tsv.TS_VARIANT_ROWWISE, 0, allowed=bits)
+    torch.cuda.synchronize()
+    assert_softmax_matches(ym.cpu().numpy(), w.logits, w.temps, what=f"rowwise masked B={B} V={V}")
+    _no_device_errors()
 
 
 def test_extreme_temperatures():

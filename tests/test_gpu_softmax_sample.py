@@ -194,3 +194,24 @@ def test_graph_capture_softmax_sample(with_probs, K):
             assert_softmax_matches(probs.cpu().numpy(), w.logits, w.temps, ref, what=f"replay {rep}")
         assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), w.uniforms, what=f"replay {rep}")
     assert tsv.ts_device_errors(device=DEV, stream=s) == 0
+
+
+@pytest.mark.parametrize("B,V,chunk", [(3, 1000, 4096), (8, 4096, 4096), (64, 16384, 4096), (128, 20480, 8192),
+                                       (2048, 32768, 8192)])
+def test_probs_of_row_kernel_shapes_come_from_the_fused_split(B, V, chunk):
+    # shapes the work-split table gives the one-workgroup-per-row kernel: the
+    # draw that also writes the probabilities takes the fused split there (it
+    # leaves the draw's group sums): its probabilities are that split's bit for
+    # bit, ts_softmax's within the tolerance, and its ids follow the rule
+    w = workloads.make(B, V, "quarters" if B >= 4 else "first16384", K=8)
+    assert tsv.ts_plan(B, V)[0] == tsv.TS_VARIANT_ROWWISE
+    x, t, u = _dev(w.logits), _dev(w.temps), _dev(w.uniforms)
+    print(f"[gpu] with-probs draw plan B={B} V={V}", flush=True)
+    ids, probs = tsv.ts_softmax_sample(x, t, u, probs_out=True)
+    fused = tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(probs, fused)
+    assert_softmax_matches(probs.cpu().numpy(), w.logits, w.temps, what=f"with probs B={B} V={V}")
+    assert_softmax_matches(tsv.ts_softmax(x, t).cpu().numpy(), w.logits, w.temps, what=f"rowwise B={B} V={V}")
+    assert_ids_valid(ids.cpu().numpy(), probs.cpu().numpy(), w.uniforms, what=f"with probs B={B} V={V}")
+    assert tsv.ts_device_errors() == 0
