@@ -57,6 +57,41 @@ def test_capture_and_replay_softmax_then_sample(variant, chunk):
     assert tsv.ts_device_errors(device=DEV, stream=s) == 0
 
 
+@pytest.mark.parametrize("B,V", [(8, 4096), (128, 20480)])
+def test_capture_short_rows_softmax_and_draw_with_probs(B, V):
+    # shapes the work-split table gives the row kernel: ts_softmax runs it (no
+    # workspace), the with-probabilities draw runs the fused split (workspace
+    # rows and partials); the reservation alone, with no call on the stream
+    # before the capture, must cover both
+    K = 16
+    s = torch.cuda.Stream(device=DEV)
+    tsv.ts_reserve(B, V, device=DEV, stream=s)
+    x = torch.zeros((B, V), dtype=torch.float32, device=DEV)
+    t = torch.ones((B,), dtype=torch.float32, device=DEV)
+    u = torch.zeros((B, K), dtype=torch.float32, device=DEV)
+    y = torch.empty_like(x)
+    yp = torch.empty_like(x)
+    ids = torch.empty((B, K), dtype=torch.int32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        tsv.ts_softmax(x, t, out=y)
+        tsv.ts_softmax_sample(x, t, u, out_ids=ids, probs_out=yp)
+    for rep in range(3):
+        w = workloads.make(B, V, "quarters", K=K, seed=2000 + rep)
+        x.copy_(torch.from_numpy(w.logits))
+        t.copy_(torch.from_numpy(w.temps))
+        u.copy_(torch.from_numpy(w.uniforms))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, what=f"rowwise replay {rep}")
+        got = yp.cpu().numpy()
+        assert_softmax_matches(got, w.logits, w.temps, what=f"with-probs replay {rep}")
+        assert_ids_valid(ids.cpu().numpy(), got, w.uniforms, what=f"with-probs replay {rep}")
+        _ = (x * 2).sum().item()
+    assert tsv.ts_device_errors(device=DEV, stream=s) == 0
+
+
 # the refused call launches nothing, so the graph torch captures is empty (by design)
 @pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 @pytest.mark.parametrize("variant,chunk", [(tsv.TS_VARIANT_FUSED, 8192), (tsv.TS_VARIANT_SPLIT, 2048)])
