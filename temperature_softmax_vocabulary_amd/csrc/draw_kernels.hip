@@ -24,7 +24,8 @@
 //    range holds the target is chosen. The target is carried into the next
 //    level's integer units in double precision and clamped to its total.
 //    Level 1 is the same for all targets of a row: ts_draw_resolve_rows
-//    computes it once per 16 targets and shares it through LDS,
+//    computes it once per 16 waves and shares it through LDS (each wave then
+//    takes 1 or 2 targets, their loads issued together: resolve_row_batch),
 //    ts_draw_resolve_waves in every wave (resolve_shares_rows picks).
 // Every wave computes the same integers from the same partials, so at each
 // level the ranges tile the total exactly. The draw follows the rule up to the
@@ -271,25 +272,99 @@ __device__ __forceinline__ void resolve_in_group(const DrawArgs& a, int64_t row,
     if (ln == e) *out = static_cast<int32_t>(col);
 }
 
-// ts_draw_resolve_rows: workgroup (row, tile) draws targets tile TW + w,
-// w < TW, of the row, one wave each. Wave 0 does level 1 once for all of them
+// Levels 2 and 3 of M targets of one row, by one wave: resolve_in_group's
+// integers for each, with every target's loads at a level issued before any
+// of them is used, so that a wave waits on memory once per level rather than
+// once per level and target. live[j] is wave-uniform and cleared for a target
+// that is done (its id, or -1, written).
+template <int KIND, int M>
+__device__ __forceinline__ void resolve_in_group_batch(const DrawArgs& a, int64_t row, float k, const int64_t (&G)[M],
+                                                       const uint64_t (&T)[M], const uint64_t (&PG)[M],
+                                                       const uint64_t (&qG)[M], bool (&live)[M],
+                                                       int32_t* const (&out)[M], int ln) {
+    const int64_t ng = a.ngroups;
+    float bw[M], gx[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {   // level 2 weights (and, from logits, the group's kept max)
+        bw[j] = live[j] ? a.bpart[(row * ng + G[j]) * kBlocksPerGroup + ln].x : 0.0f;
+        gx[j] = KIND == kDrawLogits && live[j] ? a.gpart[row * ng + G[j]].x : 0.0f;
+    }
+    uint64_t T2[M], Pb[M], qbb[M];
+    int64_t col[M];
+    int s3[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        T2[j] = 0; Pb[j] = 0; qbb[j] = 0; col[j] = 0; s3[j] = 0;
+        if (!live[j]) continue;
+        const int s2 = scale_exponent(wave_reduce<SumOp>(bw[j]));
+        const uint64_t qb = fixed_point(bw[j], s2);
+        const uint64_t incl2 = wave_inclusive_scan_u64(qb);
+        T2[j] = carry_target(T[j], PG[j], qG[j], lane_value_u64(incl2, kWave - 1));
+        const int b = find_lane(qb, incl2, 0, T2[j]);
+        if (b < 0) {   // (never, as in resolve_in_group)
+            if (ln == 0) *out[j] = -1;
+            live[j] = false;
+            continue;
+        }
+        Pb[j] = lane_value_u64(incl2 - qb, b);
+        qbb[j] = lane_value_u64(qb, b);
+        s3[j] = scale_exponent(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bw[j]), b)));
+        col[j] = G[j] * kDrawGroup + static_cast<int64_t>(b) * kDrawBlock + ln;
+    }
+    const float* xr = a.x + row * a.V;
+    const uint32_t* mrow = KIND == kDrawLogits ? draw_mask_row(a, row) : nullptr;
+    float v[M];
+    uint32_t mw[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {   // level 3 entries (and their allowed words)
+        const bool in = live[j] && col[j] < a.V;
+        v[j] = in ? xr[col[j]] : (KIND == kDrawLogits ? kNegInf : 0.0f);
+        mw[j] = mrow && in ? mrow[col[j] >> 5] : ~0u;
+    }
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        if (!live[j]) continue;
+        float e3 = v[j];
+        if constexpr (KIND == kDrawLogits) {
+            if (!((mw[j] >> (col[j] & 31)) & 1u)) e3 = kNegInf;
+            e3 = exp2_hw((e3 - guarded_shift(gx[j])) * k);   // as the partials kernel formed them
+        }
+        const uint64_t qe = fixed_point(e3, s3[j]);
+        const uint64_t incl3 = wave_inclusive_scan_u64(qe);
+        const uint64_t T3 = carry_target(T2[j], Pb[j], qbb[j], lane_value_u64(incl3, kWave - 1));
+        const int e = find_lane(qe, incl3, 0, T3);
+        if (e < 0 && ln == 0) *out[j] = -1;
+        if (ln == e) *out[j] = static_cast<int32_t>(col[j]);
+    }
+}
+
+// ts_draw_resolve_rows: workgroup (row, tile) draws targets tile TW M + j TW + w
+// (w < TW, j < M) of the row, M per wave. Wave 0 does level 1 once for all of them
 // and leaves the groups' inclusive integer prefix sums in LDS (incl[0, ng),
 // then the row's total Q at incl[ng]); each wave then finds its target's group
 // as the first with a prefix above the target, which is the group whose range
 // holds it. The integers are those of ts_draw_resolve_waves, so are the ids.
 // Dynamic LDS: 8 (ngroups + 1) bytes.
-template <int KIND>
+template <int KIND, int M>
 __global__ __launch_bounds__(kWave * kResolveRowTargets) void ts_draw_resolve_rows(DrawArgs a) {
     constexpr int TW = kResolveRowTargets;
     extern __shared__ uint64_t incl[];
     const int ln = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    const int64_t ntiles = (a.K + TW - 1) / TW;
+    const int64_t ntiles = (a.K + TW * M - 1) / (TW * M);
     const int64_t row = blockIdx.x / ntiles;
-    const int64_t kk = (blockIdx.x - row * ntiles) * TW + w;
+    const int64_t k0 = (blockIdx.x - row * ntiles) * (TW * M) + w;
     const int64_t ng = a.ngroups;
-    const bool active = kk < a.K;   // wave-uniform
-    const float u = active ? a.uniforms[row * a.K + kk] : 0.0f;
+    bool live[M];
+    float u[M];
+    int32_t* out[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const int64_t kk = k0 + static_cast<int64_t>(j) * TW;
+        live[j] = kk < a.K;   // wave-uniform
+        u[j] = live[j] ? a.uniforms[row * a.K + kk] : 0.0f;
+        out[j] = a.out_ids + row * a.K + (live[j] ? kk : 0);
+    }
     const float k = KIND == kDrawLogits ? exp2_scale(a.temps[row]) : 0.0f;
     if (w == 0) {
         RowGroups<KIND> r;
@@ -307,25 +382,38 @@ __global__ __launch_bounds__(kWave * kResolveRowTargets) void ts_draw_resolve_ro
         if (ln == 0) incl[ng] = Q;
     }
     __syncthreads();
-    if (!active) return;
-    int32_t* out = a.out_ids + row * a.K + kk;
     const uint64_t Q = incl[ng];
-    if (Q == 0) {   // nothing can be drawn
-        if (ln == 0) *out = -1;
-        return;
+    int64_t G[M];
+    uint64_t T[M], PG[M], qG[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        G[j] = 0; T[j] = 0; PG[j] = 0; qG[j] = 0;
+        if (!live[j]) continue;
+        if (Q == 0) {   // nothing can be drawn
+            if (ln == 0) *out[j] = -1;
+            live[j] = false;
+            continue;
+        }
+        T[j] = target_of(u[j], Q);
+        int64_t g = -1;
+        for (int64_t b0 = 0; b0 < ng && g < 0; b0 += kWave) {
+            const uint64_t hits = __ballot(b0 + ln < ng && incl[b0 + ln] > T[j]);
+            if (hits) g = b0 + __ffsll(static_cast<unsigned long long>(hits)) - 1;
+        }
+        if (g < 0) {   // (never: incl[ng - 1] = Q > T)
+            if (ln == 0) *out[j] = -1;
+            live[j] = false;
+            continue;
+        }
+        G[j] = g;
+        PG[j] = g > 0 ? incl[g - 1] : 0;
+        qG[j] = incl[g] - PG[j];
     }
-    const uint64_t T = target_of(u, Q);
-    int64_t G = -1;
-    for (int64_t b0 = 0; b0 < ng && G < 0; b0 += kWave) {
-        const uint64_t hits = __ballot(b0 + ln < ng && incl[b0 + ln] > T);
-        if (hits) G = b0 + __ffsll(static_cast<unsigned long long>(hits)) - 1;
+    if constexpr (M == 1) {
+        if (live[0]) resolve_in_group<KIND>(a, row, k, G[0], T[0], PG[0], qG[0], out[0], ln);
+    } else {
+        resolve_in_group_batch<KIND, M>(a, row, k, G, T, PG, qG, live, out, ln);
     }
-    if (G < 0) {   // (never: incl[ng - 1] = Q > T)
-        if (ln == 0) *out = -1;
-        return;
-    }
-    const uint64_t PG = G > 0 ? incl[G - 1] : 0;
-    resolve_in_group<KIND>(a, row, k, G, T, PG, incl[G] - PG, out, ln);
 }
 
 // ts_draw_resolve_waves (rows whose prefix sums do not fit LDS): wave w of the
@@ -405,12 +493,26 @@ hipError_t launch_draw_partials(const DrawArgs& a, int ld, int kind, hipStream_t
 
 namespace {
 
+// Targets per wave of ts_draw_resolve_rows: a wave that resolves two targets
+// issues both targets' loads together, but the grid halves; two only while
+// the grid keeps at least 4 workgroups per compute unit (two rounds of the
+// device's resident workgroups of 1024 lanes). The resolve is bound by issue
+// more than by memory waits, so four (at 5-6 waves per SIMD) was slower.
+int resolve_row_batch(int64_t B, int64_t K, int64_t cus) {
+    const int64_t per = 2 * static_cast<int64_t>(kResolveRowTargets);
+    return B * ((K + per - 1) / per) >= 4 * cus ? 2 : 1;
+}
+
 template <int KIND>
 hipError_t resolve_impl(const DrawArgs& a, hipStream_t s) {
     if (resolve_shares_rows(a.B, a.K, a.ngroups, a.cus)) {
-        const dim3 grid(static_cast<uint32_t>(a.B * ((a.K + kResolveRowTargets - 1) / kResolveRowTargets)));
+        const int M = resolve_row_batch(a.B, a.K, a.cus);
+        const int64_t per = static_cast<int64_t>(kResolveRowTargets) * M;
+        const dim3 grid(static_cast<uint32_t>(a.B * ((a.K + per - 1) / per)));
+        const dim3 block(kWave * kResolveRowTargets);
         const size_t lds = static_cast<size_t>(a.ngroups + 1) * sizeof(uint64_t);
-        hipLaunchKernelGGL((ts_draw_resolve_rows<KIND>), grid, dim3(kWave * kResolveRowTargets), lds, s, a);
+        if (M == 2) hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 2>), grid, block, lds, s, a);
+        else hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 1>), grid, block, lds, s, a);
     } else {
         const dim3 grid(static_cast<uint32_t>((a.B * a.K + DW - 1) / DW));
         hipLaunchKernelGGL((ts_draw_resolve_waves<KIND>), grid, dim3(DT), 0, s, a);

@@ -205,3 +205,39 @@ def test_rows_at_the_shared_prefix_limit(ng, K):
     assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), u, what=f"{ng} groups, logits")
     assert np.all(np.isin(ids.cpu().numpy(), cols))
     assert tsv.ts_device_errors() == 0
+
+
+@pytest.mark.parametrize("B,V,K", [(1024, 4096 + 100, 40), (512, 3 * 4096 + 7, 96)])
+def test_two_targets_per_wave_exact_and_ragged(B, V, K):
+    # Grids of at least 4 workgroups per compute unit put two targets on each
+    # wave of the shared-level-1 resolve (K = 40: the second tile has live
+    # targets only in part of its first half). Dyadic rows: every level is
+    # exact, so the ids must equal the oracle's, at and next to every CDF
+    # boundary; a row without mass gives -1 for every target; the ids-only
+    # draw from the logits, with an allowed mask, lands on allowed ids.
+    rng = np.random.default_rng(B + V + K)
+    p = np.zeros((B, V), np.float32)
+    for r in range(B):
+        ids = np.sort(rng.choice(V, size=12, replace=False))
+        p[r, ids] = np.float32(2.0) ** -rng.integers(1, 6, size=12).astype(np.float32)
+    p[3, :] = 0
+    c = np.cumsum(p.astype(np.float64), axis=1)
+    us = np.zeros((B, K), np.float32)
+    for r in range(B):
+        t = c[r, -1] if c[r, -1] > 0 else 1.0
+        cuts = np.unique(c[r]) / t
+        row = np.concatenate([cuts, np.nextafter(cuts.astype(np.float32), np.float32(0)), [0.0, 1.0]])
+        us[r] = np.resize(rng.permutation(row), K)
+    print(f"[gpu] two targets per wave B={B} V={V} K={K}", flush=True)
+    ids = _sample(p, us)
+    rows = np.arange(B) != 3   # the oracle takes rows with mass only
+    np.testing.assert_array_equal(ids[rows], sample_ref(p[rows], us[rows]))
+    assert np.all(ids[3] == -1)
+    w = workloads.make(B, V, "quarters", K=K, seed=B + K)
+    xm = torch.from_numpy(workloads.unmasked_logits(w)).to(DEV)
+    bits = torch.from_numpy(workloads.make_allowed(w).view(np.int32).copy()).to(DEV)
+    got, _ = tsv.ts_softmax_sample(xm, torch.from_numpy(w.temps).to(DEV), torch.from_numpy(w.uniforms).to(DEV),
+                                   allowed=bits)
+    torch.cuda.synchronize()
+    assert_ids_valid(got.cpu().numpy(), softmax_ref(w.logits, w.temps).astype(np.float32), w.uniforms)
+    assert tsv.ts_device_errors() == 0
