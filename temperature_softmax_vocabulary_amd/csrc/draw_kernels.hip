@@ -25,7 +25,8 @@
 //    level's integer units in double precision and clamped to its total.
 //    Level 1 is the same for all targets of a row: ts_draw_resolve_rows
 //    computes it once per 16 waves and shares it through LDS (each wave then
-//    takes 1 or 2 targets, their loads issued together: resolve_row_batch),
+//    takes 1 or 2 targets, their loads issued together: resolve_row_batch;
+//    for rows of few groups level 2 of every group is shared the same way),
 //    ts_draw_resolve_waves in every wave (resolve_shares_rows picks).
 // Every wave computes the same integers from the same partials, so at each
 // level the ranges tile the total exactly. The draw follows the rule up to the
@@ -276,17 +277,21 @@ __device__ __forceinline__ void resolve_in_group(const DrawArgs& a, int64_t row,
 // integers for each, with every target's loads at a level issued before any
 // of them is used, so that a wave waits on memory once per level rather than
 // once per level and target. live[j] is wave-uniform and cleared for a target
-// that is done (its id, or -1, written).
-template <int KIND, int M>
+// that is done (its id, or -1, written). SH: every group's level-2 integers
+// (inclusive scan, lane l for block l) and block weights are already in LDS
+// at l2i and l2w, computed by the same code, so they are the same integers.
+template <int KIND, int M, bool SH>
 __device__ __forceinline__ void resolve_in_group_batch(const DrawArgs& a, int64_t row, float k, const int64_t (&G)[M],
                                                        const uint64_t (&T)[M], const uint64_t (&PG)[M],
                                                        const uint64_t (&qG)[M], bool (&live)[M],
-                                                       int32_t* const (&out)[M], int ln) {
+                                                       int32_t* const (&out)[M], int ln,
+                                                       const uint64_t* l2i, const float* l2w) {
     const int64_t ng = a.ngroups;
     float bw[M], gx[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) {   // level 2 weights (and, from logits, the group's kept max)
-        bw[j] = live[j] ? a.bpart[(row * ng + G[j]) * kBlocksPerGroup + ln].x : 0.0f;
+        if constexpr (SH) bw[j] = live[j] ? l2w[G[j] * kWave + ln] : 0.0f;
+        else bw[j] = live[j] ? a.bpart[(row * ng + G[j]) * kBlocksPerGroup + ln].x : 0.0f;
         gx[j] = KIND == kDrawLogits && live[j] ? a.gpart[row * ng + G[j]].x : 0.0f;
     }
     uint64_t T2[M], Pb[M], qbb[M];
@@ -296,9 +301,15 @@ __device__ __forceinline__ void resolve_in_group_batch(const DrawArgs& a, int64_
     for (int j = 0; j < M; ++j) {
         T2[j] = 0; Pb[j] = 0; qbb[j] = 0; col[j] = 0; s3[j] = 0;
         if (!live[j]) continue;
-        const int s2 = scale_exponent(wave_reduce<SumOp>(bw[j]));
-        const uint64_t qb = fixed_point(bw[j], s2);
-        const uint64_t incl2 = wave_inclusive_scan_u64(qb);
+        uint64_t qb, incl2;
+        if constexpr (SH) {
+            incl2 = l2i[G[j] * kWave + ln];
+            qb = incl2 - (ln > 0 ? l2i[G[j] * kWave + ln - 1] : 0);
+        } else {
+            const int s2 = scale_exponent(wave_reduce<SumOp>(bw[j]));
+            qb = fixed_point(bw[j], s2);
+            incl2 = wave_inclusive_scan_u64(qb);
+        }
         T2[j] = carry_target(T[j], PG[j], qG[j], lane_value_u64(incl2, kWave - 1));
         const int b = find_lane(qb, incl2, 0, T2[j]);
         if (b < 0) {   // (never, as in resolve_in_group)
@@ -345,7 +356,7 @@ __device__ __forceinline__ void resolve_in_group_batch(const DrawArgs& a, int64_
 // as the first with a prefix above the target, which is the group whose range
 // holds it. The integers are those of ts_draw_resolve_waves, so are the ids.
 // Dynamic LDS: 8 (ngroups + 1) bytes.
-template <int KIND, int M>
+template <int KIND, int M, bool SH>
 __global__ __launch_bounds__(kWave * kResolveRowTargets) void ts_draw_resolve_rows(DrawArgs a) {
     constexpr int TW = kResolveRowTargets;
     extern __shared__ uint64_t incl[];
@@ -381,6 +392,17 @@ __global__ __launch_bounds__(kWave * kResolveRowTargets) void ts_draw_resolve_ro
         }
         if (ln == 0) incl[ng] = Q;
     }
+    uint64_t* l2i = incl + ng + 1;
+    float* l2w = reinterpret_cast<float*>(l2i + (SH ? ng * kWave : 0));
+    if constexpr (SH) {   // wave 1 + g: group g's level 2, for every target of the workgroup
+        const int64_t g = w - 1;
+        if (w >= 1 && g < ng) {
+            const float bw = a.bpart[(row * ng + g) * kBlocksPerGroup + ln].x;
+            const int s2 = scale_exponent(wave_reduce<SumOp>(bw));
+            l2i[g * kWave + ln] = wave_inclusive_scan_u64(fixed_point(bw, s2));
+            l2w[g * kWave + ln] = bw;
+        }
+    }
     __syncthreads();
     const uint64_t Q = incl[ng];
     int64_t G[M];
@@ -409,10 +431,10 @@ __global__ __launch_bounds__(kWave * kResolveRowTargets) void ts_draw_resolve_ro
         PG[j] = g > 0 ? incl[g - 1] : 0;
         qG[j] = incl[g] - PG[j];
     }
-    if constexpr (M == 1) {
+    if constexpr (M == 1 && !SH) {
         if (live[0]) resolve_in_group<KIND>(a, row, k, G[0], T[0], PG[0], qG[0], out[0], ln);
     } else {
-        resolve_in_group_batch<KIND, M>(a, row, k, G, T, PG, qG, live, out, ln);
+        resolve_in_group_batch<KIND, M, SH>(a, row, k, G, T, PG, qG, live, out, ln, l2i, l2w);
     }
 }
 
@@ -498,6 +520,12 @@ namespace {
 // the grid keeps at least 4 workgroups per compute unit (two rounds of the
 // device's resident workgroups of 1024 lanes). The resolve is bound by issue
 // more than by memory waits, so four (at 5-6 waves per SIMD) was slower.
+// Rows of at most this many groups (32768 columns) have every group's level 2
+// computed once per workgroup, by waves 1..ng beside wave 0's level 1, and
+// shared through LDS (12 bytes per block); longer rows compute it per target.
+constexpr int64_t kShareLevel2Groups = 8;
+static_assert(kShareLevel2Groups < kResolveRowTargets, "one wave per group besides wave 0");
+
 int resolve_row_batch(int64_t B, int64_t K, int64_t cus) {
     const int64_t per = 2 * static_cast<int64_t>(kResolveRowTargets);
     return B * ((K + per - 1) / per) >= 4 * cus ? 2 : 1;
@@ -510,9 +538,16 @@ hipError_t resolve_impl(const DrawArgs& a, hipStream_t s) {
         const int64_t per = static_cast<int64_t>(kResolveRowTargets) * M;
         const dim3 grid(static_cast<uint32_t>(a.B * ((a.K + per - 1) / per)));
         const dim3 block(kWave * kResolveRowTargets);
-        const size_t lds = static_cast<size_t>(a.ngroups + 1) * sizeof(uint64_t);
-        if (M == 2) hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 2>), grid, block, lds, s, a);
-        else hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 1>), grid, block, lds, s, a);
+        const bool sh = a.ngroups <= kShareLevel2Groups;
+        const size_t lds = static_cast<size_t>(a.ngroups + 1) * sizeof(uint64_t) +
+                           (sh ? static_cast<size_t>(a.ngroups) * kWave * (sizeof(uint64_t) + sizeof(float)) : 0);
+        if (sh) {
+            if (M == 2) hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 2, true>), grid, block, lds, s, a);
+            else hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 1, true>), grid, block, lds, s, a);
+        } else {
+            if (M == 2) hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 2, false>), grid, block, lds, s, a);
+            else hipLaunchKernelGGL((ts_draw_resolve_rows<KIND, 1, false>), grid, block, lds, s, a);
+        }
     } else {
         const dim3 grid(static_cast<uint32_t>((a.B * a.K + DW - 1) / DW));
         hipLaunchKernelGGL((ts_draw_resolve_waves<KIND>), grid, dim3(DT), 0, s, a);
