@@ -207,7 +207,8 @@ def test_rows_at_the_shared_prefix_limit(ng, K):
     assert tsv.ts_device_errors() == 0
 
 
-@pytest.mark.parametrize("B,V,K", [(1024, 4096 + 100, 40), (512, 3 * 4096 + 7, 96)])
+@pytest.mark.parametrize("B,V,K", [(1024, 4096 + 100, 40), (512, 3 * 4096 + 7, 96),
+                                   (1024, 8 * 4096, 40), (1024, 8 * 4096 + 1, 40)])   # 8 groups: level 2 shared; 9: not
 def test_two_targets_per_wave_exact_and_ragged(B, V, K):
     # Grids of at least 4 workgroups per compute unit put two targets on each
     # wave of the shared-level-1 resolve (K = 40: the second tile has live
