@@ -38,9 +38,11 @@ ts_status ts_device_memory_params(int32_t device, int32_t* clock_khz, int32_t* b
 /*
  * Number of polls (each a short sleep plus one load) a fused-kernel
  * workgroup makes while waiting for the rest of its row before it gives up,
- * raises bit 0 of the device error flags and carries on. 0 restores the
- * default (about 2^18 polls, far beyond any legal wait). Takes effect for
- * launches made after the call, on every device. For failure-path tests only.
+ * raises bit 0 of the device error flags and forms the missing chunk partials
+ * from the logits itself (the result stays exact). 0 restores the default
+ * (about 2^18 polls, far beyond any wait on a device the call has to itself).
+ * Takes effect for launches made after the call, on every device. For
+ * failure-path tests only.
  */
 ts_status ts_debug_set_spin_limit(uint32_t polls);
 

@@ -121,6 +121,100 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
     store_chunk<NT, F, VEC, true>(a.out + row * a.V, c * C, a.V, x);
 }
 
+// The payload a chunk publishes: pm in the low word, pl in the high word. pl
+// >= 0; clearing its sign bit keeps a NaN (possible only outside the method's
+// domain) from reaching the tag bit.
+__device__ __forceinline__ unsigned long long pack_partial(float pm, float pl) {
+    return (static_cast<unsigned long long>(__float_as_uint(pl) & 0x7fffffffu) << 32) | __float_as_uint(pm);
+}
+
+// One column of a chunk, as the chunk's loads and the allowed-id mask give it
+// to its lane: base = the chunk's first column, mbase = the mask word holding
+// it (or null), left = columns from base to the row's end, off = the column's
+// offset from base (-inf at or past the row's end, or where not allowed).
+__device__ __forceinline__ float chunk_value(const float* base, const uint32_t* mbase, int64_t left, uint32_t off) {
+    float v = kNegInf;
+    if (off < left) {
+        v = base[off];
+        if (mbase && !((mbase[off >> 5] >> (off & 31)) & 1u)) v = kNegInf;
+    }
+    return v;
+}
+
+// Chunk c's partial (pm, pl), formed by one wave alone and bit for bit as the
+// chunk's own workgroup forms it: the wave takes the parts of the workgroup's
+// NW waves in turn (lane l as lane 64 w + l: the same values, summed in the
+// same order), reduces each part with the same wave reduction, and combines
+// the NW sums in block_reduce's order. One column at a time and two reads of
+// the chunk (max, then sum), to keep its registers few: it runs only when a
+// wait ran out, beside the registers that hold this chunk and the next.
+template <int F>
+__device__ __forceinline__ unsigned long long chunk_partial_by_wave(const SoftmaxArgs& a, int64_t row, int64_t c,
+                                                                    float k) {
+    constexpr int C = NT * 4 * F;
+    const int l = threadIdx.x & (kWave - 1);
+    const int64_t c0 = c * C;
+    const float* base = a.logits + row * a.V + c0;
+    const uint32_t* mbase = a.allowed ? a.allowed + row * a.mwords + (c0 >> 5) : nullptr;
+    const int64_t left = a.V - c0;
+    // column of value i (group i / 4, element i % 4) of lane 64 w + l
+#define TS_LANE_COL(w, i) static_cast<uint32_t>((((i) >> 2) * NT + (w) * kWave + l) * 4 + ((i) & 3))
+    float m = kNegInf;
+#pragma unroll 1
+    for (int w = 0; w < NW; ++w) {
+#pragma unroll 1
+        for (int i = 0; i < 4 * F; ++i) m = fmaxf(m, chunk_value(base, mbase, left, TS_LANE_COL(w, i)));
+    }
+    const float pm = wave_reduce<MaxOp>(m);
+    const float sh = guarded_shift(pm);
+    float pl = 0.0f;
+#pragma unroll 1
+    for (int w = 0; w < NW; ++w) {
+        float s = 0.0f;
+#pragma unroll 1
+        for (int i = 0; i < 4 * F; ++i) s += exp2_hw((chunk_value(base, mbase, left, TS_LANE_COL(w, i)) - sh) * k);
+        const float r = wave_reduce<SumOp>(s);
+        pl = w == 0 ? r : pl + r;
+    }
+#undef TS_LANE_COL
+    return pack_partial(pm, pl);
+}
+
+// Wave 0, after a wait that ran out: the chunks whose slots were still
+// unpublished (bit j of `missing` on lane l: chunk l + 64 j) get their partial
+// from chunk_partial_by_wave, so the row combines exactly what the exchange
+// would have given it. Each slot is read once more after that chunk's loads
+// have completed, and a partial published meanwhile is taken instead: in place,
+// its owner may since have written its probabilities over the logits just read
+// (it publishes before it writes, and it writes only after a poll of its own).
+// v is parked in `park` (LDS) meanwhile, to keep registers free.
+template <int F>
+__device__ __forceinline__ void recover_missing(const SoftmaxArgs& a, int64_t row, float k,
+                                                const unsigned long long* rs, unsigned long long tag, uint32_t missing,
+                                                unsigned long long (&v)[kSlotsPerLane], unsigned long long* park) {
+    const int l = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < kSlotsPerLane; ++j) park[l + j * kWave] = v[j];
+#pragma unroll 1
+    for (int j = 0; j < kSlotsPerLane; ++j) {
+        unsigned long long lanes = __ballot((missing >> j) & 1u);
+        while (lanes) {
+            const int src = __ffsll(lanes) - 1;
+            lanes &= lanes - 1;
+            const int64_t c = src + static_cast<int64_t>(j) * kWave;
+            unsigned long long p = chunk_partial_by_wave<F>(a, row, c, k);
+            // (the loads above are complete: their values are in p; the fence
+            // keeps the slot's read from moving ahead of them)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const unsigned long long x = slot_load(rs + c);
+            if ((x & kTagBit) == tag) p = x & ~kTagBit;
+            if (l == src) park[c] = p;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kSlotsPerLane; ++j) v[j] = park[l + j * kWave];
+}
+
 // ---------------------------------------------------------------------------
 // fused: one read of the logits, one kernel.
 //
@@ -131,6 +225,9 @@ __global__ __launch_bounds__(NT) void ts_split_finalize_write(SoftmaxArgs a) {
 // the tagged slots of ts_exchange.h (no fence, no contended read-modify-write:
 // either costs microseconds per workgroup on a multi-XCD part). The host
 // launches no more workgroups than the device holds at once and at least nch.
+// Should a wait run out all the same (the device shared with work that keeps
+// some of a row's workgroups from running), recover_missing forms the missing
+// partials from the logits, so the result never depends on the wait.
 //
 // MODE kFusedProbs writes the probabilities; kFusedProbsSums also writes the
 // sums of the probabilities per group of 4096 columns (one share per wave) and
@@ -154,6 +251,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
     static_assert(MODE != kFusedProbsSums || F % 4 == 0, "draw sums need whole 4096-column groups");
     __shared__ float red[NW];
     __shared__ float chunk_scale;
+    __shared__ unsigned long long park[kSlotStride];   // a row's partials, when a wait ran out
     __shared__ float bsum[MODE == kFusedProbsSums ? F : 1][16];   // draw sums: per block of a chunk
     constexpr int C = NT * 4 * F;
     const int lane = threadIdx.x;
@@ -164,13 +262,13 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
     // mask words of the current and the next chunk: applied only when the
     // chunk's values are used, so the prefetch below never waits on its loads
     uint32_t mw[2] = {0u, 0u}, nmw[2] = {0u, 0u};
-    // lane 0: old value of the item's own slot (and of the next item's)
-    unsigned long long own = 0, next_own = 0;
+    // lane 0: old high word of the item's own slot (and of the next item's)
+    uint32_t own = 0, next_own = 0;
     {
         const int64_t row = item / a.nch, c = item - row * a.nch;
         load_chunk<NT, F, VEC, true>(a.logits + row * a.V, c * C, a.V, x, kNegInf);
         if (a.allowed) load_mask_words<NT, F>(mask_row(a, row), c * C, a.V, mw);
-        if (lane == 0) own = slot_load(a.slots + row * kSlotStride + c);
+        if (lane == 0) own = slot_load_hi(a.slots + row * kSlotStride + c);
     }
     for (; item < a.items; item += gridDim.x) {
         const int64_t row = item / a.nch;
@@ -195,10 +293,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
 
         const unsigned long long tag = next_tag(own);   // wave-uniform, all lanes
         if (lane < kWave)
-            // pl >= 0; clearing its sign bit keeps a NaN (possible only outside the
-            // method's domain) from reaching the tag bit
-            publish(rs, c, a.nch, tag,
-                    (static_cast<unsigned long long>(__float_as_uint(pl) & 0x7fffffffu) << 32) | __float_as_uint(pm));
+            publish(rs, c, a.nch, tag, pack_partial(pm, pl));
 
         // prefetch the next item (a later row: gridDim.x >= nch)
         const int64_t nitem = item + gridDim.x;
@@ -206,7 +301,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
             const int64_t nr = nitem / a.nch, nc = nitem - nr * a.nch;
             load_chunk<NT, F, VEC, true>(a.logits + nr * a.V, nc * C, a.V, nx, kNegInf);
             if (a.allowed) load_mask_words<NT, F>(mask_row(a, nr), nc * C, a.V, nmw);
-            if (lane == 0) next_own = slot_load(a.slots + nr * kSlotStride + nc);
+            if (lane == 0) next_own = slot_load_hi(a.slots + nr * kSlotStride + nc);
         }
 
         // draw sums: block sums of the exponentials, formed while the row's
@@ -225,7 +320,8 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
         if (lane < kWave) {
             unsigned long long v[kSlotsPerLane];
             const unsigned long long absent = __float_as_uint(kNegInf);   // pm = -inf, pl = 0
-            wait_row(rs, a.nch, tag, absent, v, a.spin_limit, a.err);
+            const uint32_t missing = wait_row(rs, a.nch, tag, absent, v, a.spin_limit, a.err);
+            if (__ballot(missing != 0u)) recover_missing<F>(a, row, k, rs, tag, missing, v, park);
             float mm = kNegInf;
 #pragma unroll
             for (int j = 0; j < kSlotsPerLane; ++j) mm = fmaxf(mm, __uint_as_float(static_cast<uint32_t>(v[j])));

@@ -22,8 +22,10 @@
 // Progress: a row's wait ends once all of its nch workgroups have published.
 // Kernels using this launch no more workgroups than the device holds at once
 // and at least nch, and visit items in order, so the lowest unfinished row
-// always completes. Each wait is also bounded by spin_limit polls; running
-// out raises bit 0 of *err and the caller carries on with what it has.
+// always completes. Each wait is also bounded by spin_limit polls (should the
+// device be shared with other work that keeps some of a row's workgroups from
+// running): running out raises bit 0 of *err, and wait_row reports the slots
+// still unpublished so that the caller can form their values itself.
 #pragma once
 
 #include "ts_device.h"
@@ -41,10 +43,16 @@ __device__ __forceinline__ void slot_store(unsigned long long* p, unsigned long 
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The tag to publish, from the old value of the caller's own slot (read by
+// The high word of a slot (where its tag bit sits): enough for a workgroup to
+// read the tag of its own slot, which nothing else writes.
+__device__ __forceinline__ uint32_t slot_load_hi(const unsigned long long* p) {
+    return __hip_atomic_load(reinterpret_cast<const uint32_t*>(p) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The tag to publish, from the old high word of the caller's own slot (read by
 // lane 0 before it published anything in this kernel). Wave-uniform.
-__device__ __forceinline__ unsigned long long next_tag(unsigned long long own_old) {
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(own_old >> 32));
+__device__ __forceinline__ unsigned long long next_tag(uint32_t own_old_hi) {
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(own_old_hi);
     return static_cast<unsigned long long>((hi >> 31) ^ 1u) << 63;
 }
 
@@ -57,12 +65,14 @@ __device__ __forceinline__ void publish(unsigned long long* rs, int64_t c, int64
 }
 
 // Step 3, called by all lanes of wave 0: v[j] receives slot lane + 64 j
-// (payload only) for lane + 64 j < nch, else `absent`.
-__device__ __forceinline__ void wait_row(const unsigned long long* rs, int64_t nch, unsigned long long tag,
-                                         unsigned long long absent, unsigned long long (&v)[kSlotsPerLane],
-                                         uint32_t spin_limit, uint32_t* err) {
+// (payload only) for lane + 64 j < nch, else `absent`. Returns, per lane, bit j
+// set for each of its slots that still carried the old tag when the lane's
+// polls ran out (v[j] is then `absent`, not a value of the row).
+__device__ __forceinline__ uint32_t wait_row(const unsigned long long* rs, int64_t nch, unsigned long long tag,
+                                             unsigned long long absent, unsigned long long (&v)[kSlotsPerLane],
+                                             uint32_t spin_limit, uint32_t* err) {
     const int lane = threadIdx.x;
-    uint32_t polls = 0;
+    uint32_t polls = 0, missing = 0;
 #pragma unroll
     for (int j = 0; j < kSlotsPerLane; ++j) {
         const int64_t i = lane + static_cast<int64_t>(j) * kWave;
@@ -72,14 +82,16 @@ __device__ __forceinline__ void wait_row(const unsigned long long* rs, int64_t n
             while ((x & kTagBit) != tag) {
                 if (++polls > spin_limit) {
                     __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    missing |= 1u << j;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
                 x = slot_load(rs + i);
             }
-            v[j] = x & ~kTagBit;
+            if (!((missing >> j) & 1u)) v[j] = x & ~kTagBit;
         }
     }
+    return missing;
 }
 
 }  // namespace tsk

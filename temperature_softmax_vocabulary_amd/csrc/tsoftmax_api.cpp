@@ -575,11 +575,9 @@ TS_API ts_status ts_device_errors(hipStream_t stream, uint32_t* flags) {
     for (const Alloc& a : allocs) {
         uint32_t f = 0;
         if (hipMemcpy(&f, a.base, 4, hipMemcpyDeviceToHost) != hipSuccess) return TS_ERR_HIP;
-        if (f != 0) {
-            // A timed-out wait may leave a row's slot tags out of step: clear
-            // every slot (tag 0) and flag.
-            if (hipMemset(a.base, 0, static_cast<size_t>(ws_bytes(a.bcap, a.pcap))) != hipSuccess) return TS_ERR_HIP;
-        }
+        // (a wait that ran out still leaves every slot of its row with the
+        // kernel's new tag: each workgroup publishes before it waits)
+        if (f != 0 && hipMemset(a.base, 0, sizeof(uint32_t)) != hipSuccess) return TS_ERR_HIP;
         all |= f;
     }
     *flags = all;
@@ -594,7 +592,9 @@ TS_API const char* ts_status_string(ts_status s) {
         case TS_ERR_OUT_OF_MEMORY: return "TS_ERR_OUT_OF_MEMORY: workspace allocation failed";
         case TS_ERR_NOT_RESERVED:
             return "TS_ERR_NOT_RESERVED: the stream is capturing and the workspace is too small; call ts_reserve first";
-        case TS_ERR_SYNC_TIMEOUT: return "TS_ERR_SYNC_TIMEOUT: a fused kernel's bounded wait ran out";
+        case TS_ERR_SYNC_TIMEOUT:
+            return "TS_ERR_SYNC_TIMEOUT: a fused kernel's bounded wait ran out (the missing partials were formed "
+                   "in place of it: the results are exact)";
     }
     return "unknown ts_status";
 }

@@ -3,10 +3,13 @@
 The fused kernel keeps per-row tagged slots in the stream's workspace from one
 call to the next (their parity tag flips every call). These tests change the
 chunk count per row, the row count and the vocabulary between calls on one
-stream and check every result against the oracle, and they force the bounded
-wait to run out from the host (a one-poll limit) to check that the library
-reports it, never hangs, and recovers on the next call. No kernel faults or
-hangs in any of them: a timed-out wait simply carries on.
+stream and check every result against the oracle. They also force the bounded
+wait to run out from the host (a one-poll limit): the kernel then forms the
+missing chunk partials from the logits itself, so every such call must give
+the bits of a call whose waits never ran out (for every chunk size, unaligned
+rows, an allowed-id mask, in place, and with the draw's sums), the library
+must report the slow path, and the next call must be clean. No kernel faults
+or hangs in any of them: a timed-out wait always finishes the row.
 """
 import numpy as np
 import pytest
@@ -41,32 +44,63 @@ def test_slot_tags_survive_changing_shapes_on_one_stream():
     assert tsv.ts_device_errors(device=DEV, stream=s) == 0
 
 
-def test_forced_wait_timeout_is_reported_and_recovered():
+def _timeouts(s):
+    """1 if a wait on stream s ran out since the last check, else 0."""
+    try:
+        tsv.ts_device_errors(device=DEV, stream=s)
+        return 0
+    except tsv.TsError as e:
+        assert e.status == tsv.TS_ERR_SYNC_TIMEOUT
+        return 1
+
+
+def test_forced_wait_timeout_gives_the_exact_result_and_is_reported():
     w, x, t = _case(64, 262144, 5)
+    u = torch.from_numpy(w.uniforms).to(DEV)
+    xm = torch.from_numpy(workloads.unmasked_logits(w)).to(DEV)
+    bits = torch.from_numpy(workloads.make_allowed(w).view(np.int32).copy()).to(DEV)
+    wo, xo, to = _case(8, 151937, 6)   # V % 4 = 1: unaligned rows
     ref = softmax_ref(w.logits, w.temps)
     s = torch.cuda.Stream(device=DEV)
     tsv.ts_reserve(64, 262144, device=DEV, stream=s)
+
+    def calls():
+        with torch.cuda.stream(s):
+            out = {f"fused {c}": tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, c) for c in (4096, 8192, 16384)}
+            out["masked 8192"] = tsv.ts_softmax_variant(xm, t, tsv.TS_VARIANT_FUSED, 8192, allowed=bits)
+            out["unaligned 4096"] = tsv.ts_softmax_variant(xo, to, tsv.TS_VARIANT_FUSED, 4096)
+            y = x.clone()
+            tsv.ts_softmax_variant(y, t, tsv.TS_VARIANT_FUSED, 8192, out=y)
+            out["in place 8192"] = y
+            ids, yp = tsv.ts_softmax_sample(x, t, u, probs_out=True)
+            out["with draw sums"], out["draw ids"] = yp, ids
+        s.synchronize()
+        return out
+
+    clean = calls()
+    assert _timeouts(s) == 0
     seen = 0
     try:
         tsv.ts_debug_set_spin_limit(1)
-        for _ in range(3):
-            with torch.cuda.stream(s):
-                tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, 4096)
-            try:
-                tsv.ts_device_errors(device=DEV, stream=s)
-            except tsv.TsError as e:
-                assert e.status == tsv.TS_ERR_SYNC_TIMEOUT
-                seen += 1
+        for rep in range(2):
+            got = calls()
+            seen += _timeouts(s)
+            for name, y in got.items():
+                print(f"[gpu] one-poll limit, call {rep}: {name}", flush=True)
+                assert torch.equal(y, clean[name]), f"{name}: differs from the call whose waits never ran out"
     finally:
         tsv.ts_debug_set_spin_limit(0)
     assert seen >= 1, "a one-poll wait limit never ran out"
+    for name in ("fused 8192", "in place 8192", "with draw sums"):
+        assert_softmax_matches(got[name].cpu().numpy(), w.logits, w.temps, ref, what=name)
+    assert_ids_valid(got["draw ids"].cpu().numpy(), got["with draw sums"].cpu().numpy(), w.uniforms)
+    # and the next calls run clean
     with torch.cuda.stream(s):
         y = tsv.ts_softmax_variant(x, t, tsv.TS_VARIANT_FUSED, 4096)
         y2 = tsv.ts_softmax(x, t)
     s.synchronize()
     assert tsv.ts_device_errors(device=DEV, stream=s) == 0
-    assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, ref, what="after recovery")
-    assert_softmax_matches(y2.cpu().numpy(), w.logits, w.temps, ref, what="after recovery, default plan")
+    assert torch.equal(y, clean["fused 4096"]) and torch.equal(y2, clean["fused 8192"])
 
 
 def test_two_streams_have_independent_workspaces():
