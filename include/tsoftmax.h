@@ -49,13 +49,18 @@ typedef enum ts_status {
      * workspace than ts_reserve() set aside for it; no allocation is made
      * during capture. Nothing was launched. */
     TS_ERR_NOT_RESERVED = 4,
-    /* A kernel's bounded wait for the other chunks of its row ran out
-     * (reported by ts_device_errors only). The rows it touched are invalid. */
+    /* A fused kernel's bounded wait for the other chunks of its row ran out
+     * (reported by ts_device_errors only): something else on the device kept
+     * some of the row's workgroups from running. The waiting workgroup then
+     * formed the missing chunk partials from the logits itself, bit for bit
+     * as their own workgroups form them, so the results are exact; the code
+     * reports the slow path. */
     TS_ERR_SYNC_TIMEOUT = 5
 } ts_status;
 
-/* How ts_softmax_variant splits the work (the method's chunking, bug
- * paragraph: one program per row and column chunk, then a finalize).
+/* How ts_softmax_variant splits the work. Defined by: the pull-request page,
+ * bug paragraph (one program per row and column chunk computing a running max
+ * and sum, then a finalize that combines the chunks with a global rescale).
  *   TS_VARIANT_AUTO    - pick from (B, V) with the built-in table (ts_plan).
  *   TS_VARIANT_SPLIT   - two kernels: per-chunk (max, scaled sum) partials,
  *                        then a finalize fused into the write of the probs.
@@ -69,10 +74,11 @@ typedef enum ts_status {
  *                        workspace, then writes the probs. Reads the logits
  *                        once. Rows of at most 256 chunks. Its grid is sized
  *                        to what the device holds at once; should the device be
- *                        shared with another kernel that waits on its own
- *                        co-resident workgroups, a row's wait can run out
- *                        (TS_ERR_SYNC_TIMEOUT from ts_device_errors). SPLIT
- *                        and ROWWISE never wait. */
+ *                        shared with work that keeps some of a row's
+ *                        workgroups from running, a row's wait can run out:
+ *                        the waiting workgroup then forms the missing partials
+ *                        itself (exact result, reported as TS_ERR_SYNC_TIMEOUT
+ *                        by ts_device_errors). SPLIT and ROWWISE never wait. */
 typedef enum ts_variant {
     TS_VARIANT_AUTO = 0,
     TS_VARIANT_SPLIT = 1,
@@ -82,6 +88,12 @@ typedef enum ts_variant {
 
 /*
  * probs[b, :] = softmax(logits[b, :] / temps[b]) for b in [0, B).
+ *
+ * Defined by: the pull-request page, test paragraph (each row divided by its
+ * own temperature, then a softmax over the vocabulary, checked against
+ * torch.softmax) and fix paragraph (a column chunk whose leading block is all
+ * -inf adds nothing; a fully masked chunk contributes 0 to the rescaled sum,
+ * so the row stays finite while it keeps a finite logit).
  *
  * logits : [B, V] float32, row-major, contiguous (row pitch V elements).
  *          Entries are finite or -inf (masked). Each row must keep at least
@@ -106,10 +118,13 @@ ts_status ts_softmax(const float* logits, const float* temps, int64_t B, int64_t
                      float* out, hipStream_t stream);
 
 /*
- * ts_softmax with an allowed-token mask applied as the logits are read: the
- * mask producers of the scope paragraph (allowed token ids, min-tokens,
- * grammar) mark ids as not allowed, and such an id is treated exactly as a -inf
- * logit, without a separate pass that writes -inf into the logits.
+ * ts_softmax with an allowed-token mask applied as the logits are read.
+ *
+ * Defined by: the pull-request page, scope paragraph (allowed-token-ids,
+ * min_tokens and grammar masks are what write -inf into the logits) and the
+ * test paragraph (the softmax they feed). A disallowed id is treated exactly as
+ * a -inf logit, without a separate pass that writes -inf into the logits; the
+ * bit layout is this library's.
  *
  * allowed : [B, ceil(V / 32)] uint32, row-major. Id j of row b is allowed when
  *           bit (j % 32) of allowed[b * ceil(V / 32) + j / 32] is 1; bits past
@@ -124,7 +139,11 @@ ts_status ts_softmax_masked(const float* logits, const float* temps, const uint3
 
 /*
  * ts_softmax (allowed == NULL) or ts_softmax_masked with the work split
- * forced: `variant` is a ts_variant and `chunk` the columns per workgroup (one
+ * forced. Defined by: the pull-request page, bug paragraph (the per-chunk
+ * partial and the finalize) and the A/B list (finite rows give the same bits
+ * for every kernel configuration with and without the -inf guard, which the
+ * tests check over these splits). `variant` is a ts_variant and `chunk` the
+ * columns per workgroup (one
  * of 1024, 2048, 4096, 8192, 16384 for SPLIT and FUSED; ignored by ROWWISE;
  * 0 = the table's choice). Same result contract. Meant for tests and tuning; a
  * combination the library cannot run (e.g. FUSED with more chunks per row than
@@ -135,7 +154,10 @@ ts_status ts_softmax_variant(const float* logits, const float* temps, const uint
 
 /*
  * The work split ts_softmax would use for (B, V) on the current device, for a
- * 16-byte aligned call with V % 4 == 0. Host only: launches nothing. A row
+ * 16-byte aligned call with V % 4 == 0. Host only: launches nothing. Defined
+ * by: the pull-request page, A/B script and timing table (the kernel
+ * configuration is chosen per shape, there by the autotuner; here by a table
+ * measured on MI355X). A row
  * takes the fused split only if the device holds all of its chunks at once;
  * with no HIP device present, that check is skipped (the table alone).
  * variant, chunk : host pointers, written on TS_OK.
@@ -146,6 +168,12 @@ ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
 
 /*
  * Inverse-CDF token draws from caller-supplied uniforms.
+ *
+ * Defined by: the pull-request page, scope paragraph (the sampler consumes the
+ * temperature softmax) and results table, sampling row (every draw lands on an
+ * allowed id: 1024 of 1024 draws over 16 rows x 64). The page does not give the
+ * draw's rule; inverse CDF on caller-supplied uniforms is this library's
+ * reading.
  *
  * probs    : [B, V] float32 row-major contiguous, non-negative rows (normally
  *            ts_softmax outputs). Entries that are not > 0 (0, negative, NaN)
@@ -159,10 +187,12 @@ ts_status ts_plan(int64_t B, int64_t V, int32_t* variant, int32_t* chunk);
  *            groups' float sums at one power-of-two scale per row, the
  *            chosen group's block sums at one scale, then the chosen block's
  *            entries at one scale, each in 64-bit fixed point. Inside a block
- *            the choice is exact; a group or block boundary can sit about
- *            1e-7 of the row total away from the exact one (exact when every
- *            entry is a multiple of one power of two that the sums hold
- *            exactly). The id is always one with a positive entry. A row
+ *            the choice is exact; a group or block boundary sits at most
+ *            (gamma_12 + gamma_6) / 2 = 5.4e-7 of the row total from the
+ *            exact one, gamma_n = n 2^-24 / (1 - n 2^-24) bounding the float
+ *            sums over a group (tree depth 12) and a block (depth 6); exact
+ *            when every entry is a multiple of one power of two that the sums
+ *            hold exactly. The id is always one with a positive entry. A row
  *            with no positive entry (or a sum that is not finite) gives -1.
  * Errors   : TS_ERR_INVALID_ARGUMENT for B < 0, K < 0, V < 1,
  *            V > INT32_MAX, a NULL pointer when B*K > 0, or out_ids overlapping
@@ -173,11 +203,11 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
 
 /*
  * The softmax and the token draw in one call: ts_softmax followed by
- * ts_sample. Without probs_out the probabilities are never written: the logits
- * are read once for per-group and per-block partials, and only the 64-id
- * blocks that hold a target are read again. The draw consumes the softmax as in the scope
- * paragraph of the pull-request page; every id drawn has a finite logit
- * (results table, sampling row).
+ * ts_sample. Defined by: the pull-request page, scope paragraph (the sampler
+ * consumes the softmax) and results table, sampling row (every id drawn has a
+ * finite logit). Without probs_out the probabilities are never written: the
+ * logits are read once for per-group and per-block partials, and only the
+ * 64-id blocks that hold a target are read again.
  *
  * logits, temps : as for ts_softmax.
  * allowed       : NULL, or an allowed-id bitmask as for ts_softmax_masked.
@@ -194,8 +224,14 @@ ts_status ts_sample(const float* probs, const float* uniforms, int64_t B, int64_
  *                 same three levels of integer prefix sums; every id
  *                 drawn has a finite logit (and an allowed bit); -1 for a row
  *                 with none. With probs_out the draw reads the written
- *                 probabilities; without, it works from the logits (one read
- *                 of them in all).
+ *                 probabilities (boundaries within 6.9e-7 of the row total of
+ *                 those probabilities' exact CDF: the sums are formed before
+ *                 scaling, tree depths 14 and 7, and each written value is
+ *                 rounded once more); without, it works from the logits (one
+ *                 read of them in all), and the float32 exponents add their
+ *                 error: at most 3 ln(2) 2^-24 |d| + 5 2^-24 relative per
+ *                 entry, |d| its distance below the row's max in log2 units,
+ *                 averaged over the row's probabilities.
  * Errors        : as ts_softmax and ts_sample. K == 0 reduces to ts_softmax
  *                 (or a no-op when probs_out is NULL).
  */
@@ -204,6 +240,9 @@ ts_status ts_softmax_sample(const float* logits, const float* temps, const uint3
                             int32_t* out_ids, hipStream_t stream);
 
 /*
+ * Not defined by the pages: workspace management. It follows the pattern of
+ * the n-gram hash page's "capture-safe" item (fixed shapes, no host reads, no
+ * allocation inside a captured replay) so that calls can be captured.
  * Set aside the workspace for any later call with B <= max_B and
  * V <= max_V on `stream`, so that those calls allocate nothing (needed
  * before capturing them into a HIP graph). Allocates and clears device
@@ -217,17 +256,19 @@ ts_status ts_softmax_sample(const float* logits, const float* temps, const uint3
 ts_status ts_reserve(int64_t max_B, int64_t max_V, hipStream_t stream);
 
 /*
+ * Not defined by the pages: diagnostics of this library's fused kernel.
  * Synchronise `stream`, then report and clear the device-side error flags of
  * its workspace. *flags (host pointer) receives the raw bits (bit 0: a fused
- * kernel's bounded wait ran out). Returns TS_ERR_SYNC_TIMEOUT if bit 0 was
- * set, else TS_OK.
+ * kernel's bounded wait ran out, and the kernel formed the missing partials
+ * itself: the results are exact, the call took the slow path). Returns
+ * TS_ERR_SYNC_TIMEOUT if bit 0 was set, else TS_OK.
  */
 ts_status ts_device_errors(hipStream_t stream, uint32_t* flags);
 
-/* Static text for a status code (never NULL). */
+/* Not defined by the pages. Static text for a status code (never NULL). */
 const char* ts_status_string(ts_status status);
 
-/* TSOFTMAX_ABI_VERSION of the built library. */
+/* Not defined by the pages. TSOFTMAX_ABI_VERSION of the built library. */
 int32_t ts_abi_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,7 @@ import torch
 import temperature_softmax_vocabulary_amd as tsv
 from oracle import softmax_masked_ref, softmax_ref
 from temperature_softmax_vocabulary_amd import workloads
-from tests.parity import assert_ids_valid, assert_softmax_matches
+from tests.parity import assert_ids_valid, assert_logit_ids_valid, assert_softmax_matches
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -105,9 +105,10 @@ def test_softmax_sample_with_mask_draws_only_allowed_ids():
     ids, probs = tsv.ts_softmax_sample(xd, td, torch.from_numpy(w.uniforms).to(DEV), probs_out=True,
                                        allowed=_bits(bits))
     torch.cuda.synchronize()
-    assert_softmax_matches(probs.cpu().numpy(), w.logits, w.temps, ref, what="masked softmax_sample")
+    p = probs.cpu().numpy()
+    assert_softmax_matches(p, w.logits, w.temps, ref, what="masked softmax_sample")
     ids = ids.cpu().numpy()
-    assert_ids_valid(ids, ref.astype(np.float32), w.uniforms, what="masked draw")
+    assert_ids_valid(ids, p, w.uniforms, what="masked draw")
     keep = np.isfinite(w.logits)
     assert np.all(keep[np.arange(w.B)[:, None], ids])
 
@@ -123,5 +124,5 @@ def test_ids_only_draw_with_mask_draws_only_allowed_ids():
         torch.cuda.synchronize()
         assert none is None
         ids = ids.cpu().numpy()
-        assert_ids_valid(ids, ref.astype(np.float32), w.uniforms, what=f"{name} ids only, masked")
+        assert_logit_ids_valid(ids, w.logits, w.temps, w.uniforms, ref, what=f"{name} ids only, masked")
         assert np.all(np.isfinite(w.logits)[np.arange(w.B)[:, None], ids])

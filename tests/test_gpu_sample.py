@@ -3,7 +3,10 @@
 The probabilities fed to both sides come from the oracle (cast to float32),
 never from the HIP softmax. Several ids are correct when a target sits within
 rounding of a CDF boundary, so the unique part is compared: the id has p > 0
-and owns the target up to 1e-5 in the oracle's CDF. Where every CDF value is
+and owns the target in the oracle's CDF of the same probabilities, up to the
+band tests/parity.py derives from the draw's float32 sums (6.9e-7 of the row
+total; ids drawn from logits: a per-row band that adds the float32 exponents'
+error). Where every CDF value is
 exact (dyadic weights) the ids must equal the oracle's exactly. The page's
 draw case ("fix(kernel): avoid nan in triton sampling softmax when a chunk
 starts with -inf", results table, sampling row: 3 allowed ids, 16 rows x 64
@@ -19,7 +22,7 @@ import torch
 import temperature_softmax_vocabulary_amd as tsv
 from oracle import sample_ref, softmax_ref
 from temperature_softmax_vocabulary_amd import workloads
-from tests.parity import assert_ids_valid
+from tests.parity import assert_ids_valid, assert_logit_ids_valid
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -201,8 +204,7 @@ def test_rows_at_the_shared_prefix_limit(ng, K):
     ids, _ = tsv.ts_softmax_sample(torch.from_numpy(x).to(DEV), torch.from_numpy(t).to(DEV),
                                    torch.from_numpy(u).to(DEV))
     torch.cuda.synchronize()
-    ref = softmax_ref(x, t)
-    assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), u, what=f"{ng} groups, logits")
+    assert_logit_ids_valid(ids.cpu().numpy(), x, t, u, what=f"{ng} groups, logits")
     assert np.all(np.isin(ids.cpu().numpy(), cols))
     assert tsv.ts_device_errors() == 0
 
@@ -240,5 +242,5 @@ def test_two_targets_per_wave_exact_and_ragged(B, V, K):
     got, _ = tsv.ts_softmax_sample(xm, torch.from_numpy(w.temps).to(DEV), torch.from_numpy(w.uniforms).to(DEV),
                                    allowed=bits)
     torch.cuda.synchronize()
-    assert_ids_valid(got.cpu().numpy(), softmax_ref(w.logits, w.temps).astype(np.float32), w.uniforms)
+    assert_logit_ids_valid(got.cpu().numpy(), w.logits, w.temps, w.uniforms, what="two per wave, masked")
     assert tsv.ts_device_errors() == 0

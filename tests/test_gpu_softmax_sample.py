@@ -1,9 +1,12 @@
 """GPU parity of ts_softmax_sample (softmax and inverse-CDF draw in one call).
 
 The probabilities must pass the same gates as ts_softmax against the float64
-oracle; the ids, with and without the probabilities written, are checked
-against the oracle's own probabilities and CDF (the unique part: p > 0 and the
-target inside the id's CDF interval up to 1e-5). The two modes weigh groups and
+oracle. The ids are checked for the unique part (p > 0 and the target inside
+the id's interval of the exact CDF): those drawn with the probabilities written
+against the CDF of what was written, within the band the draw's float32 sums
+allow; those drawn straight from the logits against the oracle's probabilities,
+within a per-row band that adds the float32 exponents' error (tests/parity.py
+derives both). The two modes weigh groups and
 blocks from different float sums, so they agree except within rounding of a
 boundary. The page's draw case ("fix(kernel): avoid nan in triton sampling
 softmax when a chunk starts with -inf", results table, sampling row) must give
@@ -19,7 +22,7 @@ import torch
 import temperature_softmax_vocabulary_amd as tsv
 from oracle import sample_ref, softmax_ref
 from temperature_softmax_vocabulary_amd import workloads
-from tests.parity import assert_ids_valid, assert_softmax_matches
+from tests.parity import SAMPLE_TAU, assert_ids_valid, assert_logit_ids_valid, assert_softmax_matches
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -45,10 +48,14 @@ def test_configs_probs_and_ids(name):
     ids = ids.cpu().numpy()
     ids_only = ids_only.cpu().numpy()
     # ids-only draws from group partials of the logits, the other from the
-    # written probabilities: both follow the rule, and can differ only for a
-    # target within float rounding of a group boundary
-    for got, what in ((ids, "with probs"), (ids_only, "ids only")):
-        assert_ids_valid(got, ref.astype(np.float32), w.uniforms, what=f"{name} {what}")
+    # written probabilities: both follow the rule (each against what it drew
+    # from, within its derived band), and can differ only for a target within
+    # float rounding of a boundary
+    dev_p = assert_ids_valid(ids, p, w.uniforms, what=f"{name} with probs")
+    dev_l, tau_l = assert_logit_ids_valid(ids_only, w.logits, w.temps, w.uniforms, ref, what=f"{name} ids only")
+    print(f"[gpu] {name}: largest target outside its exact interval: with probs {dev_p:.2e} "
+          f"(band {SAMPLE_TAU:.2e}), ids only {dev_l:.2e} (band up to {tau_l:.2e})", flush=True)
+    for got in (ids, ids_only):
         assert np.all(np.isfinite(w.logits)[np.arange(w.B)[:, None], got])
     assert np.mean(ids == ids_only) > 0.99
     # The draw uses the GPU's fp32 probabilities (relative error ~1e-6), so a
@@ -73,8 +80,8 @@ def test_matches_separate_softmax_then_sample():
     assert_softmax_matches(probs_f.cpu().numpy(), w.logits, w.temps, ref, what="fused with draw")
     assert_softmax_matches(probs_s.cpu().numpy(), w.logits, w.temps, ref, what="separate")
     a, b = ids_f.cpu().numpy(), ids_s.cpu().numpy()
-    assert_ids_valid(a, ref.astype(np.float32), w.uniforms, what="fused")
-    assert_ids_valid(b, ref.astype(np.float32), w.uniforms, what="separate")
+    assert_ids_valid(a, probs_f.cpu().numpy(), w.uniforms, what="fused")
+    assert_ids_valid(b, probs_s.cpu().numpy(), w.uniforms, what="separate")
     assert np.mean(a == b) > 0.99
 
 
@@ -94,8 +101,9 @@ def test_odd_shapes(B, V, K):
     ref = softmax_ref(w.logits, w.temps)
     ids, probs = tsv.ts_softmax_sample(_dev(w.logits), _dev(w.temps), _dev(w.uniforms), probs_out=True)
     torch.cuda.synchronize()
-    assert_softmax_matches(probs.cpu().numpy(), w.logits, w.temps, ref, what=f"B={B} V={V}")
-    assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), w.uniforms, what=f"B={B} V={V} K={K}")
+    p = probs.cpu().numpy()
+    assert_softmax_matches(p, w.logits, w.temps, ref, what=f"B={B} V={V}")
+    assert_ids_valid(ids.cpu().numpy(), p, w.uniforms, what=f"B={B} V={V} K={K}")
 
 
 def test_in_place_probs_and_extreme_uniforms():
@@ -132,7 +140,7 @@ def test_long_rows_draw_from_logits():
     w = workloads.make(2, 2097152 + 4099, "block20000", K=32)
     ref = softmax_ref(w.logits, w.temps)
     ids = tsv.ts_softmax_sample(_dev(w.logits), _dev(w.temps), _dev(w.uniforms))[0].cpu().numpy()
-    assert_ids_valid(ids, ref.astype(np.float32), w.uniforms, what="long rows")
+    assert_logit_ids_valid(ids, w.logits, w.temps, w.uniforms, ref, what="long rows")
 
 
 def test_with_probs_ids_agree_with_ts_sample_on_them():
@@ -191,8 +199,11 @@ def test_graph_capture_softmax_sample(with_probs, K):
         torch.cuda.synchronize()
         ref = softmax_ref(w.logits, w.temps)
         if with_probs:
-            assert_softmax_matches(probs.cpu().numpy(), w.logits, w.temps, ref, what=f"replay {rep}")
-        assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), w.uniforms, what=f"replay {rep}")
+            p = probs.cpu().numpy()
+            assert_softmax_matches(p, w.logits, w.temps, ref, what=f"replay {rep}")
+            assert_ids_valid(ids.cpu().numpy(), p, w.uniforms, what=f"replay {rep}")
+        else:
+            assert_logit_ids_valid(ids.cpu().numpy(), w.logits, w.temps, w.uniforms, ref, what=f"replay {rep}")
     assert tsv.ts_device_errors(device=DEV, stream=s) == 0
 
 

@@ -17,7 +17,7 @@ import torch
 import temperature_softmax_vocabulary_amd as tsv
 from oracle import softmax_ref
 from temperature_softmax_vocabulary_amd import workloads
-from tests.parity import assert_ids_valid, assert_softmax_matches
+from tests.parity import assert_ids_valid, assert_logit_ids_valid, assert_softmax_matches
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -91,11 +91,13 @@ def test_odd_vocabulary_default_plan_and_draws(V):
     ids_l, _ = tsv.ts_softmax_sample(x, t, u)
     ids_w, p2 = tsv.ts_softmax_sample(x, t, u, probs_out=True)
     torch.cuda.synchronize()
-    assert_softmax_matches(y.cpu().numpy(), w.logits, w.temps, ref, what=f"V={V}")
+    yh, p2h = y.cpu().numpy(), p2.cpu().numpy()
+    assert_softmax_matches(yh, w.logits, w.temps, ref, what=f"V={V}")
     # (with the draw the softmax may run another chunk size: equal to rounding)
-    assert_softmax_matches(p2.cpu().numpy(), w.logits, w.temps, ref, what=f"V={V} with draw")
-    for ids, what in ((ids_p, "sample"), (ids_l, "ids only"), (ids_w, "with probs")):
-        assert_ids_valid(ids.cpu().numpy(), ref.astype(np.float32), w.uniforms, what=f"V={V} {what}")
+    assert_softmax_matches(p2h, w.logits, w.temps, ref, what=f"V={V} with draw")
+    assert_ids_valid(ids_p.cpu().numpy(), yh, w.uniforms, what=f"V={V} sample")
+    assert_ids_valid(ids_w.cpu().numpy(), p2h, w.uniforms, what=f"V={V} with probs")
+    assert_logit_ids_valid(ids_l.cpu().numpy(), w.logits, w.temps, w.uniforms, ref, what=f"V={V} ids only")
     assert tsv.ts_device_errors() == 0
 
 
