@@ -483,9 +483,10 @@ def main(argv=None) -> int:
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--extras", choices=("all", "copy", "none"), default="all",
+    ap.add_argument("--extras", choices=("all", "copy", "draws", "none"), default="all",
                     help="side measurements after the timed region: all, only the copy "
-                         "(the counter runs' calibration), or none")
+                         "(the counter runs' calibration), the copy and the eager draw calls "
+                         "(the draw kernels' counter runs: no graph is captured), or none")
     ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
     ap.add_argument("--ab-guard", action="store_true",
                     help="instead of the JSON line: the page's A/B (builds with and without the -inf "
@@ -609,7 +610,14 @@ def main(argv=None) -> int:
     }
 
     extras = {}
-    if args.extras in ("all", "copy"):
+
+    def leg(name):
+        # names the leg on stderr before it starts, so that a run that ends
+        # early (e.g. under a profiler) shows where
+        print(f"[bench] leg {name}", file=sys.stderr, flush=True)
+
+    if args.extras in ("all", "copy", "draws"):
+        leg("copy")
         # same bytes through a plain streaming copy, cold (practical ceiling,
         # and the byte-counter calibration of the profile runs)
         def cp(i):
@@ -621,9 +629,26 @@ def main(argv=None) -> int:
         extras["copy_us_per_call"] = round(cus, 3)
         extras["copy_GBps"] = round(bytes_per_call / cus / 1e3, 1)
         extras["softmax_over_copy"] = round(cus / us, 4)
+    if args.extras in ("all", "draws"):
+        # token draws on the same rows, 64 uniforms each (not part of the metric):
+        # ts_sample on written probabilities, and the one-pass softmax + draw
+        # with and without writing the probabilities (cold, rotating sets; eager)
+        u = torch.from_numpy(w.uniforms).to(dev)
+        ids = torch.empty((B, w.uniforms.shape[1]), dtype=torch.int32, device=dev)
+        leg("draw: ts_sample")
+        extras["sample_us_per_call"] = round(
+            _side_us(torch, lambda i: tsv.ts_sample(ys[i % nsets], u, out_ids=ids)), 3)
+        leg("draw: ids only")
+        extras["softmax_sample_ids_only_us_per_call"] = round(
+            _side_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids)), 3)
+        leg("draw: with probabilities")
+        extras["softmax_sample_with_probs_us_per_call"] = round(
+            _side_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids,
+                                                            probs_out=ys[i % nsets])), 3)
     if args.extras == "all":
         # the softmax and the same-bytes copy in 7 interleaved runs of 200 cold
         # calls each: medians, and the median of the per-run ratios
+        leg("interleaved")
         runs = []
         for _ in range(7):
             runs.append((_elapsed_us(torch, step, 200), _elapsed_us(torch, cp, 200)))
@@ -632,10 +657,13 @@ def main(argv=None) -> int:
             "copy_us_median": round(statistics.median(r[1] for r in runs), 3),
             "softmax_over_copy_median": round(statistics.median(r[1] / r[0] for r in runs), 4)}
         # hot: the same buffers every call (how the page timed, graph replays of one input)
+        leg("hot")
+
         def hot(i):
             step(0)
         extras["hot_us_per_call"] = round(_side_us(torch, hot), 3)
         # graph replay of the same rotating calls (launch gaps removed)
+        leg("graph")
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         tsv.ts_reserve(B, V, stream=s)
@@ -656,18 +684,6 @@ def main(argv=None) -> int:
         e1.record()
         torch.cuda.synchronize()
         extras["graph_us_per_call"] = round(e0.elapsed_time(e1) * 1000.0 / (reps * nsets * 8), 3)
-        # token draws on the same rows, 64 uniforms each (not part of the metric):
-        # ts_sample on written probabilities, and the one-pass softmax + draw
-        # with and without writing the probabilities (cold, rotating sets)
-        u = torch.from_numpy(w.uniforms).to(dev)
-        ids = torch.empty((B, w.uniforms.shape[1]), dtype=torch.int32, device=dev)
-        extras["sample_us_per_call"] = round(
-            _side_us(torch, lambda i: tsv.ts_sample(ys[i % nsets], u, out_ids=ids)), 3)
-        extras["softmax_sample_ids_only_us_per_call"] = round(
-            _side_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids)), 3)
-        extras["softmax_sample_with_probs_us_per_call"] = round(
-            _side_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids,
-                                                            probs_out=ys[i % nsets])), 3)
         # the same masks applied from an allowed-id bitmask while the logits are read
         # (finite logits everywhere, B * ceil(V/32) * 4 extra bytes read)
         # (cold like the timed region: the logit and mask buffers rotate too)
@@ -679,11 +695,14 @@ def main(argv=None) -> int:
         def masked(i):
             j = i % nsets
             tsv.ts_softmax_masked(xms[j], ts[j], bitss[j], out=ys[j])
+        leg("bitmask")
         extras["masked_bitmask_us_per_call"] = round(_side_us(torch, masked), 3)
         del xms, bitss
         # every workload, graph replay (the small ones are launch-bound)
+        leg("workloads by graph replay")
         extras["configs_graph_us_per_call"] = configs_graph_us(torch, tsv, workloads, dev)
         # the draws on every workload (64 uniforms per row), graph replay
+        leg("draws on every workload by graph replay")
         extras["configs_graph_draw_us_per_call"] = {
             name: {op: graph_cold_us(torch, tsv, dev, workloads.make_config(name), op)
                    for op in ("sample", "ids", "probs")}
