@@ -118,6 +118,29 @@ ts_status ts_softmax(const float* logits, const float* temps, int64_t B, int64_t
                      float* out, hipStream_t stream);
 
 /*
+ * ts_softmax for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, work split, kernels and result (bit for bit) as ts_softmax, but
+ * it never allocates: instead of the per-stream workspace it uses one
+ * 4 MiB + 256 B device array that the library holds on each GPU until the
+ * process ends (fused-kernel slots for up to 1024 rows, split partials for up
+ * to 262144 (row, chunk) pairs). Every call on a GPU shares that GPU's array
+ * whatever its stream, so calls that overlap on one GPU race: keep them on one
+ * stream, or otherwise ordered. The array needs no clearing between calls.
+ * Its bounded-wait flag is not reported (ts_device_errors covers the
+ * workspaces only); a wait that runs out still gives the exact result.
+ * Errors : as ts_softmax, plus TS_ERR_INVALID_ARGUMENT when the call's work
+ *          split needs more than the array holds: the fused split with more
+ *          than 1024 rows, or the split pair with more than 262144 - B
+ *          (row, chunk) pairs. Calls that take the one-workgroup-per-row
+ *          kernel need no scratch and have no such limit. TS_ERR_HIP if the
+ *          array's address cannot be looked up (done once per device, on the
+ *          first call with that device current).
+ */
+ts_status ts_softmax_noalloc(const float* logits, const float* temps, int64_t B, int64_t V,
+                             float* out, hipStream_t stream);
+
+/*
  * ts_softmax with an allowed-token mask applied as the logits are read.
  *
  * Defined by: the pull-request page, scope paragraph (allowed-token-ids,

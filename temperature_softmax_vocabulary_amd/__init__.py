@@ -33,6 +33,7 @@ from .binding import (  # noqa: F401
     ts_sample,
     ts_softmax,
     ts_softmax_masked,
+    ts_softmax_noalloc,
     ts_softmax_sample,
     ts_softmax_variant,
     ts_status_string,

@@ -40,6 +40,7 @@ CHUNKS = (1024, 2048, 4096, 8192, 16384)
 _P, _I64, _I32, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
 SIGNATURES = {
     "ts_softmax": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "ts_softmax_noalloc": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "ts_softmax_masked": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P]),
     "ts_softmax_variant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _I32, _I32, _P]),
     "ts_plan": (ctypes.c_int, [_I64, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
@@ -160,6 +161,20 @@ def ts_softmax(logits: torch.Tensor, temps: torch.Tensor, out: Optional[torch.Te
     with _on(logits.device):
         _check(lib().ts_softmax(logits.data_ptr(), temps.data_ptr(), B, V, out.data_ptr(),
                                 _stream_handle(logits.device, stream)))
+    return out
+
+
+def ts_softmax_noalloc(logits: torch.Tensor, temps: torch.Tensor, out: torch.Tensor,
+                       stream=None) -> torch.Tensor:
+    """ts_softmax through the entry point that allocates no device memory (its
+    scratch is one array per GPU, shared by every call on it: overlapping calls
+    race). out is required (it may be logits)."""
+    if out is None:
+        raise ValueError("ts_softmax_noalloc needs out: it allocates nothing")
+    B, V, out = _softmax_args(logits, temps, out)
+    with _on(logits.device):
+        _check(lib().ts_softmax_noalloc(logits.data_ptr(), temps.data_ptr(), B, V, out.data_ptr(),
+                                        _stream_handle(logits.device, stream)))
     return out
 
 

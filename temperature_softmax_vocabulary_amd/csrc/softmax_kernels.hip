@@ -19,11 +19,40 @@
 //            for the row's other chunks, then writes (logits read once).
 //  rowwise : one workgroup per row; the row sits in registers when it fits
 //            (read once), else an online (m, l) sweep and a write sweep.
+#include <map>
+#include <mutex>
+
 #include "ts_device.h"
 #include "ts_exchange.h"
 #include "ts_launch.h"
 
 namespace tsk {
+
+// Scratch of the allocation-free entry point (ts_softmax_noalloc): flags,
+// fused-kernel slots, split partials, as ts_launch.h lays them out. Zero when
+// the library loads, so every slot starts with tag 0 (the exchange needs only
+// that a row's slots carry one tag between kernels, which every kernel keeps).
+// Each GPU holds its own copy until the process ends. Host code uses the
+// address static_scratch returns, never this name.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+    static std::mutex mu;
+    static std::map<int, void*> addr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = addr.find(dev);
+    if (it == addr.end()) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        it = addr.emplace(dev, p).first;
+    }
+    *ptr = it->second;
+    return hipSuccess;
+}
 
 namespace {
 

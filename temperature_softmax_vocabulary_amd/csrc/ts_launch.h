@@ -109,4 +109,14 @@ bool resolve_shares_rows(int64_t B, int64_t K, int64_t ngroups, int64_t cus);
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, bool vec, hipStream_t s);
 
+// The allocation-free entry point's scratch: one device array per GPU, laid
+// out as a workspace with kStaticRows rows of fused-kernel slots and
+// kStaticParts split partials (flags, then slots, then partials).
+constexpr int64_t kStaticRows = 1024;
+constexpr int64_t kStaticParts = 262144;
+constexpr int64_t kStaticScratchBytes = 256 + 8 * kSlotStride * kStaticRows * kSlotSets + 8 * kStaticParts;
+// The array's device address on the current device (looked up once per
+// device, with that device current).
+hipError_t static_scratch(void** ptr);
+
 }  // namespace tsk

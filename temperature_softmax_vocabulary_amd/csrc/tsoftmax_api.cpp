@@ -463,6 +463,23 @@ TS_API ts_status ts_softmax(const float* logits, const float* temps, int64_t B, 
     return run_softmax(logits, temps, nullptr, B, V, out, TS_VARIANT_AUTO, 0, stream);
 }
 
+TS_API ts_status ts_softmax_noalloc(const float* logits, const float* temps, int64_t B, int64_t V, float* out,
+                                    hipStream_t stream) {
+    if (!sizes_ok(B, V)) return TS_ERR_INVALID_ARGUMENT;
+    if (B == 0) return TS_OK;
+    SoftmaxCall call;
+    ts_status st = prepare_softmax(logits, temps, nullptr, B, V, out, TS_VARIANT_AUTO, 0, &call);
+    if (st != TS_OK) return st;
+    if (call.plan.variant == TS_VARIANT_ROWWISE) return launch_softmax(call, WsView{}, false, nullptr, stream);
+    if (call.need_b > tsk::kStaticRows || call.need_p > tsk::kStaticParts) return TS_ERR_INVALID_ARGUMENT;
+    void* base = nullptr;
+    if (tsk::static_scratch(&base) != hipSuccess) return TS_ERR_HIP;
+    static_assert(tsk::kStaticScratchBytes == 256 + 8 * tsk::kSlotStride * tsk::kStaticRows * tsk::kSlotSets +
+                                                  8 * tsk::kStaticParts,
+                  "the scratch is laid out as a workspace of kStaticRows rows and kStaticParts partials");
+    return launch_softmax(call, ws_view(Alloc{base, tsk::kStaticRows, tsk::kStaticParts}), false, nullptr, stream);
+}
+
 TS_API ts_status ts_softmax_masked(const float* logits, const float* temps, const uint32_t* allowed, int64_t B,
                                    int64_t V, float* out, hipStream_t stream) {
     if (B > 0 && !allowed) return TS_ERR_INVALID_ARGUMENT;
