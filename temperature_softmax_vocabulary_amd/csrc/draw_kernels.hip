@@ -9,12 +9,13 @@
 //
 // A row is cut into groups of 4096 columns, each of 64 blocks of 64 columns,
 // and the draw takes two short kernels:
-//  ts_draw_partials: one read of the row, no exchange between workgroups. Each
-//    group gets a float partial: from logits, the method's chunk partial
-//    (pm, pl) -- the group's max and the sum of exp2((x - shift) k) with the
-//    -inf guard of the fix paragraph; from probabilities, the sum of the
-//    positive entries (one share per wave). Each block gets its sum of the
-//    same terms: the exponentials at its group's max, or the probabilities.
+//  ts_draw_partials: one read of the row, one workgroup per group, no
+//    exchange between workgroups. Each group gets a float partial: from
+//    logits, the method's chunk partial (pm, pl) -- the group's max and the sum
+//    of exp2((x - shift) k) with the -inf guard of the fix paragraph; from
+//    probabilities, the sum of the positive entries. Each block gets its sum of
+//    the same terms: the exponentials at its group's max, or the
+//    probabilities; the group's sum is the sum of its block sums.
 //  the resolve: one wave per (row, target), three levels. At each level the
 //    64 lanes hold 64 float weights -- the row's groups (for logits, their pl
 //    rescaled to the row's max as in the finalize, so that a fully masked
@@ -44,107 +45,65 @@ namespace {
 
 constexpr int DT = 256;                  // lanes per workgroup
 constexpr int DW = DT / kWave;
-static_assert(DT * 4 * 4 == kDrawGroup, "a group is four float4 per lane");
+static_assert(DT * 4 * 4 == kDrawGroup && DW == 4, "a group is four float4 per lane of four waves");
 static_assert(kBlocksPerGroup == kWave && kDrawBlock == kWave, "one lane per block, one lane per entry");
 
 __device__ __forceinline__ const uint32_t* draw_mask_row(const DrawArgs& a, int64_t row) {
     return a.allowed ? a.allowed + row * a.mwords : nullptr;
 }
 
-// N sums (or maxima) over the workgroup at once: one LDS round for all of
-// them, combined in a fixed order; every lane gets every result.
-template <class Op, int NW, int N>
-__device__ __forceinline__ void block_reduce_n(float (&v)[N], float (*lds)[NW]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const float w = wave_reduce<Op>(v[i]);
-        if ((threadIdx.x & (kWave - 1)) == 0) lds[i][threadIdx.x / kWave] = w;
-    }
-    __syncthreads();
-    Op op;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        float r = lds[i][0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) r = op(r, lds[i][w]);
-        v[i] = r;
-    }
-    __syncthreads();
-}
-
 // ---------------------------------------------------------------------------
-// ts_draw_partials: workgroup (row, h) reads groups G = GPW h + d, d < GPW, in
-// the layout of load_chunk (F = 4 GPW: chunk group j = columns
-// GPW h 4096 + j 1024 + [0, 1024), lane t holding 4 consecutive columns of
-// each), so group G = GPW h + j / 4 and its block b = 16 (j % 4) + t / 16 is
-// one row of 16 lanes.
+// ts_draw_partials: one workgroup per group of 4096 columns (item = row
+// ngroups + group). Lane t holds the float4 at column 1024 j + 4 t of the
+// group (the layout of load_chunk, j < 4), so block 16 j + t / 16 is one row
+// of 16 lanes. The block sums meet in LDS and leave in one 256-byte store;
+// the group's sum is the sum of its block sums.
 // ---------------------------------------------------------------------------
-template <int LD, int KIND, int GPW>
+template <int LD, int KIND>
 __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
-    __shared__ float red[GPW][DW];   // (logits only)
-    constexpr int F = 4 * GPW;
+    constexpr int F = kDrawGroup / (DT * 4);
+    __shared__ float red[DW];                 // (logits: the group's max)
+    __shared__ float blocks[kBlocksPerGroup];
     const int t = threadIdx.x;
-    const int64_t nh = (a.ngroups + GPW - 1) / GPW;
-    const int64_t row = blockIdx.x / nh;
-    const int64_t h = blockIdx.x - row * nh;
-    const int64_t G0 = h * GPW;
-    const bool holder = (t & 15) == 15;
+    const int64_t item = blockIdx.x;
+    const int64_t row = item / a.ngroups;
+    const int64_t c0 = (item - row * a.ngroups) * kDrawGroup;
+    const bool masked = KIND == kDrawLogits && a.allowed;
     float x[4 * F];
+    uint32_t mw[2];
+    issue_chunk_loads<DT, F, LD, true>(a.x + row * a.V, c0, a.V, x);
+    if (masked) load_mask_words<DT, F>(draw_mask_row(a, row), c0, a.V, mw);
+    if (c0 + kDrawGroup > a.V) {   // (workgroup-uniform: the row's last, partial group)
+        if constexpr (LD == kLdUnaligned) shift_tail_group<DT, F>(c0, a.V, x);
+        fill_past_end<DT, F>(c0, a.V, x, KIND == kDrawLogits ? kNegInf : 0.0f);
+    }
+    float gm = 0.0f;
     if constexpr (KIND == kDrawLogits) {
-        {
-            const int64_t c0 = G0 * kDrawGroup;
-            const uint32_t* mrow = draw_mask_row(a, row);
-            uint32_t mw[2];
-            issue_chunk_loads<DT, F, LD, true>(a.x + row * a.V, c0, a.V, x);
-            if (mrow) load_mask_words<DT, F>(mrow, c0, a.V, mw);
-            if constexpr (LD == kLdUnaligned) shift_tail_group<DT, F>(c0, a.V, x);
-            fill_past_end<DT, F>(c0, a.V, x, kNegInf);
-            if (mrow) apply_mask_words<DT, F>(c0, a.V, mw, x);
-        }
+        if (masked) apply_mask_words<DT, F>(c0, a.V, mw, x);
+        // the method's chunk partial for the group: its max, then the sum of
+        // exp2((x - shift) k) with the -inf guard; the blocks sum the same terms
+        float m = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4 * F; ++i) m = fmaxf(m, x[i]);
+        m = wave_reduce<MaxOp>(m);
+        if ((t & (kWave - 1)) == 0) red[t / kWave] = m;
+        __syncthreads();   // (red is written once: no barrier after its reads)
+        gm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        const float gsh = guarded_shift(gm);
         const float k = exp2_scale(a.temps[row]);
-        // each group's max over the workgroup; then its exponentials at that max,
-        // summed per block and per group as probabilities are
-        float gm[GPW];
 #pragma unroll
-        for (int d = 0; d < GPW; ++d) {
-            float m = kNegInf;
-#pragma unroll
-            for (int i = 16 * d; i < 16 * d + 16; ++i) m = fmaxf(m, x[i]);
-            gm[d] = m;
-        }
-        block_reduce_n<MaxOp, DW, GPW>(gm, red);
-        float gl[GPW];
-#pragma unroll
-        for (int d = 0; d < GPW; ++d) {
-            const float gsh = guarded_shift(gm[d]);
-#pragma unroll
-            for (int i = 16 * d; i < 16 * d + 16; ++i) x[i] = exp2_hw((x[i] - gsh) * k);
-            const int64_t G = G0 + d;   // (workgroup-uniform test: a group past the row's end writes nothing)
-            gl[d] = G < a.ngroups ? prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup)
-                                  : 0.0f;
-        }
-        block_reduce_n<SumOp, DW, GPW>(gl, red);
-#pragma unroll
-        for (int d = 0; d < GPW; ++d)
-            if (t == 0 && G0 + d < a.ngroups) a.gpart[row * a.ngroups + G0 + d] = make_float4(gm[d], gl[d], 0.0f, 0.0f);
+        for (int i = 0; i < 4 * F; ++i) x[i] = exp2_hw((x[i] - gsh) * k);
     } else {
-        issue_chunk_loads<DT, F, LD, true>(a.x + row * a.V, G0 * kDrawGroup, a.V, x);
-        if constexpr (LD == kLdUnaligned) shift_tail_group<DT, F>(G0 * kDrawGroup, a.V, x);
-        fill_past_end<DT, F>(G0 * kDrawGroup, a.V, x, 0.0f);
-        float gs[GPW];
 #pragma unroll
-        for (int d = 0; d < GPW; ++d) {
-            const int64_t G = G0 + d;   // (workgroup-uniform test: a group past the row's end writes nothing)
-            gs[d] = G < a.ngroups ? prob_block_sums<F>(x, 4 * d, a.bpart + (row * a.ngroups + G) * kBlocksPerGroup)
-                                  : 0.0f;
-        }
-        // each wave's share of each group sum (kernel-wide no barrier)
-#pragma unroll
-        for (int d = 0; d < GPW; ++d) {
-            const float w = wave_reduce<SumOp>(gs[d]);
-            if ((t & (kWave - 1)) == 0 && G0 + d < a.ngroups)
-                reinterpret_cast<float*>(a.gpart + row * a.ngroups + G0 + d)[t / kWave] = w;
-        }
+        for (int i = 0; i < 4 * F; ++i) x[i] = fmaxf(x[i], 0.0f);   // NaN and negatives hold no mass
+    }
+    block_sums_to_lds<F>(x, blocks);
+    __syncthreads();
+    if (t < kWave) {
+        const float b = blocks[t];
+        a.bpart[item * kBlocksPerGroup + t] = b;
+        const float g = wave_reduce<SumOp>(b);
+        if (t == 0) a.gpart[item] = KIND == kDrawLogits ? make_float4(gm, g, 0.0f, 0.0f) : make_float4(g, 0.0f, 0.0f, 0.0f);
     }
 }
 
@@ -238,7 +197,7 @@ __device__ __forceinline__ void resolve_in_group(const DrawArgs& a, int64_t row,
     const int64_t ng = a.ngroups;
     // level 2: the group's 64 blocks, lane l holding block l
     // (block weights: sums of the group's exponentials at its max, or of probabilities)
-    const float bw = a.bpart[(row * ng + G) * kBlocksPerGroup + ln].x;
+    const float bw = a.bpart[(row * ng + G) * kBlocksPerGroup + ln];
     const int s2 = scale_exponent(wave_reduce<SumOp>(bw));   // > 0: qG >= 1 needs a positive group
     const uint64_t qb = fixed_point(bw, s2);
     const uint64_t incl2 = wave_inclusive_scan_u64(qb);
@@ -291,7 +250,7 @@ __device__ __forceinline__ void resolve_in_group_batch(const DrawArgs& a, int64_
 #pragma unroll
     for (int j = 0; j < M; ++j) {   // level 2 weights (and, from logits, the group's kept max)
         if constexpr (SH) bw[j] = live[j] ? l2w[G[j] * kWave + ln] : 0.0f;
-        else bw[j] = live[j] ? a.bpart[(row * ng + G[j]) * kBlocksPerGroup + ln].x : 0.0f;
+        else bw[j] = live[j] ? a.bpart[(row * ng + G[j]) * kBlocksPerGroup + ln] : 0.0f;
         gx[j] = KIND == kDrawLogits && live[j] ? a.gpart[row * ng + G[j]].x : 0.0f;
     }
     uint64_t T2[M], Pb[M], qbb[M];
@@ -397,7 +356,7 @@ __global__ __launch_bounds__(kWave * kResolveRowTargets) void ts_draw_resolve_ro
     if constexpr (SH) {   // wave 1 + g: group g's level 2, for every target of the workgroup
         const int64_t g = w - 1;
         if (w >= 1 && g < ng) {
-            const float bw = a.bpart[(row * ng + g) * kBlocksPerGroup + ln].x;
+            const float bw = a.bpart[(row * ng + g) * kBlocksPerGroup + ln];
             const int s2 = scale_exponent(wave_reduce<SumOp>(bw));
             l2i[g * kWave + ln] = wave_inclusive_scan_u64(fixed_point(bw, s2));
             l2w[g * kWave + ln] = bw;
@@ -482,26 +441,12 @@ __global__ __launch_bounds__(DT) void ts_draw_resolve_waves(DrawArgs a) {
     resolve_in_group<KIND>(a, row, k, G, T, PG, qG, out, ln);
 }
 
-// Groups per workgroup of the partials kernel: two (32 KiB of reads) once the
-// call fills the device, else one.
-constexpr int kPartialsGPW = 2;
-
-template <int LD, int GPW>
+template <int LD>
 hipError_t partials_impl(const DrawArgs& a, int kind, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(a.B * ((a.ngroups + GPW - 1) / GPW)));
-    if (kind == kDrawLogits) hipLaunchKernelGGL((ts_draw_partials<LD, kDrawLogits, GPW>), grid, dim3(DT), 0, s, a);
-    else hipLaunchKernelGGL((ts_draw_partials<LD, kDrawProbs, GPW>), grid, dim3(DT), 0, s, a);
+    const dim3 grid(static_cast<uint32_t>(a.B * a.ngroups));
+    if (kind == kDrawLogits) hipLaunchKernelGGL((ts_draw_partials<LD, kDrawLogits>), grid, dim3(DT), 0, s, a);
+    else hipLaunchKernelGGL((ts_draw_partials<LD, kDrawProbs>), grid, dim3(DT), 0, s, a);
     return hipGetLastError();
-}
-
-template <int GPW>
-hipError_t partials_ld(const DrawArgs& a, int ld, int kind, hipStream_t s) {
-    switch (ld) {
-        case kLdAligned: return partials_impl<kLdAligned, GPW>(a, kind, s);
-        case kLdUnaligned: return partials_impl<kLdUnaligned, GPW>(a, kind, s);
-        case kLdScalar: return partials_impl<kLdScalar, GPW>(a, kind, s);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 }  // namespace
@@ -509,8 +454,12 @@ hipError_t partials_ld(const DrawArgs& a, int ld, int kind, hipStream_t s) {
 hipError_t launch_draw_partials(const DrawArgs& a, int ld, int kind, hipStream_t s) {
     // the unaligned loads need a row of at least 4 columns
     if (ld == kLdUnaligned && a.V < 4) ld = kLdScalar;
-    const bool wide = a.B * a.ngroups >= 2048;
-    return wide ? partials_ld<kPartialsGPW>(a, ld, kind, s) : partials_ld<1>(a, ld, kind, s);
+    switch (ld) {
+        case kLdAligned: return partials_impl<kLdAligned>(a, kind, s);
+        case kLdUnaligned: return partials_impl<kLdUnaligned>(a, kind, s);
+        case kLdScalar: return partials_impl<kLdScalar>(a, kind, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 namespace {

@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NT, (FusedOcc<F, MODE>::waves_per_eu)) void ts_fuse
             const int64_t g0 = c * NG;   // the chunk's first group
             const int64_t gbase = row * a.ngroups + g0;
             if (lane < 16 * F && g0 + (lane >> 6) < a.ngroups)
-                a.bpart[gbase * kBlocksPerGroup + lane] = make_float2((&bsum[0][0])[lane] * scale, 0.0f);
+                a.bpart[gbase * kBlocksPerGroup + lane] = (&bsum[0][0])[lane] * scale;
             if (lane < NG * NW) {
                 const int d = lane / NW, w = lane % NW;
                 if (g0 + d < a.ngroups) {

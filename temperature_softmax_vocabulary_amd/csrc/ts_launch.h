@@ -52,7 +52,7 @@ struct SoftmaxArgs {
                            // more than kSplitRowCombineMin chunks [B] (shift, 1 / sum)
     float4* gpart;         // fused with draw sums: [B * ngroups] per group, the sums of
                            // its probabilities held by each of the 4 waves
-    float2* bpart;         // fused with draw sums: [B * ngroups * 64] (sum of probs, 0) per block
+    float* bpart;          // fused with draw sums: [B * ngroups * 64] sum of probs per block
     int64_t ngroups;       // groups of kDrawGroup columns per row (fused with draw sums)
     unsigned long long* slots;   // [B * kSlotStride] tagged (pm, pl) slots of the fused kernel
     uint32_t* err;         // device error flags (bit 0: a bounded wait ran out)
@@ -87,7 +87,7 @@ struct DrawArgs {
     int32_t* out_ids;         // [B, K]
     float4* gpart;            // [B, ngroups] group partials: (max, sum exp2, 0, 0) from logits,
                               // or the positive sums held by each of the 4 waves
-    float2* bpart;            // [B, ngroups, 64] block partials: (sum, 0) of the exponentials at the
+    float* bpart;             // [B, ngroups, 64] block partials: sum of the exponentials at the
                               // group's max, or of the positive probabilities
     int64_t B;
     int64_t V;

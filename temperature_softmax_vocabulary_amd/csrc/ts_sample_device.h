@@ -75,33 +75,24 @@ __device__ __forceinline__ uint64_t wave_inclusive_scan_u64(uint64_t v) {
 // Sum over the 64 lanes of a wave, returned to every lane.
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) { return lane_value_u64(wave_inclusive_scan_u64(v), 63); }
 
-// A group's weight from its probability partials: the four waves' sums, added
-// in one fixed order.
+// A group's weight from its probability partials (a float4 per group): the
+// sum of its four parts, added in one fixed order (the fused softmax leaves one
+// part per wave; the draw's partials kernel the whole sum and three zeros).
 __device__ __forceinline__ float group_prob_sum(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 
-// Block sums of probabilities for one group of a chunk held in the layout of
-// load_chunk with 256 lanes: the group is the four 1024-column chunk groups
-// j0 .. j0 + 3, and block b = 16 (j - j0) + t / 16 is the 4 entries of each of
-// the 16 lanes of one row of lanes. Writes (sum, 0) of every block to bgroup[b]
-// from the row's last lane and returns that lane's share of the group sum (0
-// on the other lanes). Both the fused softmax (on the probabilities it writes)
-// and the draw's partials kernel (on given probabilities) sum this way, so the
-// same probabilities give the same sums.
+// Block sums of one group held in the layout of load_chunk with 256 lanes and
+// F = 4: block b = 16 j + t / 16 is the 4 entries of each of the 16 lanes of
+// one row of lanes in chunk group j. The last lane of each row of lanes writes
+// the block's sum to blocks[b] (LDS); the caller synchronises before reading.
 template <int F>
-__device__ __forceinline__ float prob_block_sums(const float (&p)[4 * F], int j0, float2* __restrict__ bgroup) {
+__device__ __forceinline__ void block_sums_to_lds(const float (&x)[4 * F], float* blocks) {
+    static_assert(F == 4, "a group of 4096 columns is four float4 per lane");
     const int t = threadIdx.x;
-    const bool holder = (t & 15) == 15;
-    float bs[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int j = j0 + jj;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = p[4 * j + e] > 0.0f ? p[4 * j + e] : 0.0f;
-        bs[jj] = row16_reduce<SumOp>((y[0] + y[1]) + (y[2] + y[3]));
-        if (holder) bgroup[jj * 16 + (t >> 4)] = make_float2(bs[jj], 0.0f);
+    for (int j = 0; j < F; ++j) {
+        const float b = row16_reduce<SumOp>((x[4 * j] + x[4 * j + 1]) + (x[4 * j + 2] + x[4 * j + 3]));
+        if ((t & 15) == 15) blocks[j * 16 + (t >> 4)] = b;
     }
-    return holder ? (bs[0] + bs[1]) + (bs[2] + bs[3]) : 0.0f;
 }
 
 }  // namespace tsk

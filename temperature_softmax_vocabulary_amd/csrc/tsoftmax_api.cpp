@@ -393,7 +393,7 @@ ts_status launch_softmax(SoftmaxCall& call, const WsView& v, bool group_sums, bo
                 grid = fused_grid(a.items, a.nch, cap);
                 a.ngroups = cdiv(a.V, tsk::kDrawGroup);
                 a.gpart = reinterpret_cast<float4*>(v.part);
-                a.bpart = v.part + 2 * a.B * a.ngroups;
+                a.bpart = reinterpret_cast<float*>(v.part + 2 * a.B * a.ngroups);
                 *sums = true;
             }
         }
@@ -417,9 +417,9 @@ ts_status run_softmax(const float* logits, const float* temps, const uint32_t* a
     return launch_softmax(call, ws_view(*w), false, nullptr, stream);
 }
 
-// Workspace partials of a draw, in float2 units: per row, one float4 per group
-// of 4096 columns, then 64 float2 per group (its blocks of 64 columns).
-int64_t draw_parts(int64_t B, int64_t V) { return B * cdiv(V, tsk::kDrawGroup) * (2 + tsk::kBlocksPerGroup); }
+// Workspace partials of a draw, in float2 units: one float4 per group of 4096
+// columns, then 64 floats per group (its blocks of 64 columns).
+int64_t draw_parts(int64_t B, int64_t V) { return B * cdiv(V, tsk::kDrawGroup) * (2 + tsk::kBlocksPerGroup / 2); }
 
 // The draw's two kernels (draw_kernels.hip) on x = logits (kDrawLogits) or
 // probabilities (kDrawProbs); partials_done: the partials are already in the
@@ -441,7 +441,7 @@ ts_status launch_draw(int kind, const float* x, const float* temps, const uint32
     ts_status st = device_cus(&d.cus);
     if (st != TS_OK) return st;
     d.gpart = reinterpret_cast<float4*>(v.part);
-    d.bpart = v.part + 2 * B * d.ngroups;
+    d.bpart = reinterpret_cast<float*>(v.part + 2 * B * d.ngroups);
     const int ld = aligned16(x) && (V % 4 == 0) ? tsk::kLdAligned : tsk::kLdUnaligned;
     if (!partials_done) {
         hipError_t e = tsk::launch_draw_partials(d, ld, kind, stream);

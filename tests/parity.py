@@ -28,14 +28,14 @@ the exact ones, derived from the float32 arithmetic the draw does:
     and 6; the draw-sums of the fused softmax at 14 and 7, plus one rounding of
     each written probability): SAMPLE_TAU = 6.9e-7.
   * ids drawn straight from the logits (ts_softmax_sample without
-    probabilities), against the oracle's probabilities: the sums (depth 13 and
+    probabilities), against the oracle's probabilities: the sums (depth 12 and
     6) plus the float32 exponents. An exponent d = (x - gsh) log2(e) / T carries
     at most 3 roundings (difference, scale, product): relative error 3 ln(2) u
     |d| in 2^d, plus 2u for the hardware exp2, in the element and again in its
     group's rescale (where the two |d| add up to the element's distance from
     the row's max), plus u for the rescale's product. A boundary moves by at
     most the mass-weighted mean of those errors, so per row
-    tau = (gamma(13) + gamma(6)) / 2 + 3 ln(2) u E_p[|d|] + 5u, with E_p[|d|]
+    tau = (gamma(12) + gamma(6)) / 2 + 3 ln(2) u E_p[|d|] + 5u, with E_p[|d|]
     taken from the oracle (ids_only_tau).
 """
 import math
@@ -75,7 +75,7 @@ def mean_log2_distance(ref: np.ndarray, logits: np.ndarray, temps: np.ndarray) -
 def ids_only_tau(ref: np.ndarray, logits: np.ndarray, temps: np.ndarray) -> np.ndarray:
     """Per-row band for ids drawn straight from the logits, checked against the
     oracle's probabilities (module docstring)."""
-    return (gamma(13) + gamma(6)) / 2 + 3 * LN2 * U32 * mean_log2_distance(ref, logits, temps) + 5 * U32
+    return (gamma(12) + gamma(6)) / 2 + 3 * LN2 * U32 * mean_log2_distance(ref, logits, temps) + 5 * U32
 
 
 def softmax_errors(got: np.ndarray, logits: np.ndarray, ref: np.ndarray) -> dict:

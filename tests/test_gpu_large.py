@@ -94,7 +94,7 @@ def _check_draws(x, t, ids, us, rows, from_logits):
         total = _mass(xr, T, xmax, 0, V)
         e = _mean_log2_distance(xr, T, xmax, total)
         if from_logits:
-            tau = (gamma(13) + gamma(6)) / 2 + 3 * LN2 * U32 * e + 5 * U32
+            tau = (gamma(12) + gamma(6)) / 2 + 3 * LN2 * U32 * e + 5 * U32
         else:
             tau = SAMPLE_TAU + 3 * LN2 * U32 * e + 7 * U32
         for k, u in enumerate(us):
