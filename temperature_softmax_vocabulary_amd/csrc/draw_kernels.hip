@@ -65,9 +65,12 @@ __global__ __launch_bounds__(DT) void ts_draw_partials(DrawArgs a) {
     __shared__ float red[DW];                 // (logits: the group's max)
     __shared__ float blocks[kBlocksPerGroup];
     const int t = threadIdx.x;
+    // (32-bit: the grid is; a 64-bit division would hold up the first loads)
+    const uint32_t ng = static_cast<uint32_t>(a.ngroups);
+    const uint32_t row32 = blockIdx.x / ng;
     const int64_t item = blockIdx.x;
-    const int64_t row = item / a.ngroups;
-    const int64_t c0 = (item - row * a.ngroups) * kDrawGroup;
+    const int64_t row = row32;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x - row32 * ng) * kDrawGroup;
     const bool masked = KIND == kDrawLogits && a.allowed;
     float x[4 * F];
     uint32_t mw[2];
