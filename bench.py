@@ -209,12 +209,13 @@ def _side_us(torch, fn, n=500, reps=3, warmup=30):
     return statistics.median(_elapsed_us(torch, fn, n) for _ in range(reps))
 
 
-def graph_cold_us(torch, tsv, dev, w, op: str = "softmax") -> float:
+def graph_cold_us(torch, tsv, dev, w, op: str = "softmax", reps: int = 5) -> float:
     """µs per call, cold, from graph replay (launch gaps removed): rotating
-    slices of one >= 512 MiB buffer pair, all captured into one graph. op:
-    "softmax" (ts_softmax), "copy" (the same-bytes copy), "sample" (ts_sample
-    on the slices' probabilities), "ids" and "probs" (ts_softmax_sample
-    without and with writing the probabilities), with w's uniforms."""
+    slices of one >= 512 MiB buffer pair, all captured into one graph and
+    replayed `reps` times. op: "softmax" (ts_softmax), "copy" (the same-bytes
+    copy), "sample" (ts_sample on the slices' probabilities), "ids" and
+    "probs" (ts_softmax_sample without and with writing the probabilities),
+    with w's uniforms."""
     B, V = w.B, w.V
     nsets = min(512, max(2, math.ceil((512 << 20) / (2 * B * V * 4))))
     x = torch.from_numpy(w.logits).to(dev).unsqueeze(0).repeat(nsets, 1, 1)
@@ -250,7 +251,6 @@ def graph_cold_us(torch, tsv, dev, w, op: str = "softmax") -> float:
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 5
     e0.record()
     for _ in range(reps):
         g.replay()
@@ -483,10 +483,12 @@ def main(argv=None) -> int:
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--extras", choices=("all", "copy", "draws", "none"), default="all",
+    ap.add_argument("--extras", choices=("all", "copy", "draws", "draws-graph", "none"), default="all",
                     help="side measurements after the timed region: all, only the copy "
                          "(the counter runs' calibration), the copy and the eager draw calls "
-                         "(the draw kernels' counter runs: no graph is captured), or none")
+                         "(the draw kernels' counter runs: no graph is captured), the draws "
+                         "by graph replay only (the draw kernels' trace: every kernel queued "
+                         "behind the one before, as in a busy stream), or none")
     ap.add_argument("--no-extras", action="store_true", help="same as --extras none")
     ap.add_argument("--ab-guard", action="store_true",
                     help="instead of the JSON line: the page's A/B (builds with and without the -inf "
@@ -645,6 +647,12 @@ def main(argv=None) -> int:
         extras["softmax_sample_with_probs_us_per_call"] = round(
             _side_us(torch, lambda i: tsv.ts_softmax_sample(xs[i % nsets], ts[i % nsets], u, out_ids=ids,
                                                             probs_out=ys[i % nsets])), 3)
+    if args.extras == "draws-graph":
+        # the three draws by graph replay (cold): each call's kernels start as
+        # the previous call's end, with no host gap between them
+        leg("draws by graph replay")
+        extras["graph_draw_us_per_call"] = {
+            op: graph_cold_us(torch, tsv, dev, w, op, reps=40) for op in ("sample", "ids", "probs")}
     if args.extras == "all":
         # the softmax and the same-bytes copy in 7 interleaved runs of 200 cold
         # calls each: medians, and the median of the per-run ratios
